@@ -1,0 +1,172 @@
+"""CPU oracle of the temporal module -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  It wraps ``oracle.c`` (plain fp64 C, see
+``oracle.h`` for the passages each routine follows) with ctypes over numpy
+arrays.  Inputs are float32 arrays (dt = F32) or uint16 bf16 bit patterns
+(dt = BF16) shaped [F, H, W, C] (or [F, S, C]); outputs are float64 arrays
+[F, n_locs, C] for the requested spatial locations (flattened h*W + w).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so (always recompiles)."""
+    tmp = _SO + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread",
+                           os.path.join(_HERE, "oracle.c"), "-o", tmp, "-lm"])
+    os.replace(tmp, _SO)
+    return _SO
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i64, d, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int
+        L.oracle_gn_stats.argtypes = [vp, i, i64, i64, i64, i64, d, vp, vp, vp, i]
+        L.oracle_groupnorm.argtypes = [vp, i, i64, i64, i64, i64, d, vp, vp, vp, i64, vp, vp, vp, i]
+        L.oracle_conv3.argtypes = [vp, vp, vp, vp, vp, i, i64, i64, i64, vp, i64, vp, i]
+        L.oracle_dda_keys.argtypes = [i64, i64, i, i, vp]
+        L.oracle_dda.argtypes = [vp, vp, vp, i, i64, i64, i64, i, i, i, d, vp, i64, vp, i]
+        L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, vp, i64, vp, vp, vp, vp, vp, i]
+        L.oracle_round_to.argtypes = [d, i]
+        L.oracle_round_to.restype = d
+        for fn in ("oracle_gn_stats", "oracle_groupnorm", "oracle_conv3", "oracle_dda_keys", "oracle_dda",
+                   "oracle_chain"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs are float32 or uint16 bf16 bits, got {a.dtype}")
+
+
+def _c(a):
+    return None if a is None else np.ascontiguousarray(a)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _locs(locs, S):
+    if locs is None:
+        locs = np.arange(S, dtype=np.int64)
+    return np.ascontiguousarray(np.asarray(locs, dtype=np.int64))
+
+
+def _fsc(x):
+    if x.ndim == 4:
+        F, H, W, C = x.shape
+        return F, H * W, C
+    F, S, C = x.shape
+    return F, S, C
+
+
+def gn_stats(x, G, eps=1e-5, nthreads=0):
+    """(mean[G], var[G], rstd[G]) over the whole tensor, fp64."""
+    x = _c(x)
+    F, S, C = _fsc(x)
+    mean, var, rstd = (np.empty(G) for _ in range(3))
+    rc = lib().oracle_gn_stats(_ptr(x), _dt(x), F, S, C, G, eps, _ptr(mean), _ptr(var), _ptr(rstd), nthreads)
+    if rc:
+        raise ValueError(f"oracle_gn_stats rc={rc}")
+    return mean, var, rstd
+
+
+def groupnorm(x, G, eps=1e-5, gamma=None, beta=None, locs=None, nthreads=0):
+    """(y[F, n_locs, C], mean[G], rstd[G])."""
+    x = _c(x)
+    F, S, C = _fsc(x)
+    locs = _locs(locs, S)
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float64)
+    b = None if beta is None else np.ascontiguousarray(beta, dtype=np.float64)
+    y = np.empty((F, locs.size, C))
+    mean, rstd = np.empty(G), np.empty(G)
+    rc = lib().oracle_groupnorm(_ptr(x), _dt(x), F, S, C, G, eps, _ptr(g), _ptr(b), _ptr(locs), locs.size,
+                                _ptr(y), _ptr(mean), _ptr(rstd), nthreads)
+    if rc:
+        raise ValueError(f"oracle_groupnorm rc={rc}")
+    return y, mean, rstd
+
+
+def conv3(x, w, ctx_pre=None, ctx_post=None, bias=None, locs=None, nthreads=0):
+    """y[F, n_locs, C] of the kernel-3 temporal conv; w is [3, C_out, C_in]."""
+    x, w, ctx_pre, ctx_post = _c(x), _c(w), _c(ctx_pre), _c(ctx_post)
+    F, S, C = _fsc(x)
+    assert w.shape == (3, C, C) and w.dtype == x.dtype
+    for c in (ctx_pre, ctx_post):
+        assert c is None or (c.size == S * C and c.dtype == x.dtype)
+    locs = _locs(locs, S)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    y = np.empty((F, locs.size, C))
+    rc = lib().oracle_conv3(_ptr(x), _ptr(ctx_pre), _ptr(ctx_post), _ptr(w), _ptr(b), _dt(x), F, S, C,
+                            _ptr(locs), locs.size, _ptr(y), nthreads)
+    if rc:
+        raise ValueError(f"oracle_conv3 rc={rc}")
+    return y
+
+
+def dda_keys(F, t, n_local=16, n_global=16):
+    keys = np.empty(n_local + n_global, dtype=np.int64)
+    n = lib().oracle_dda_keys(F, t, n_local, n_global, _ptr(keys))
+    return keys[:n].copy()
+
+
+def dda(q, k, v, head_dim=64, n_local=16, n_global=16, scale=0.0, locs=None, nthreads=0):
+    """o[F, n_locs, C] of dual-domain attention (scale <= 0 means 1/sqrt(head_dim))."""
+    q, k, v = _c(q), _c(k), _c(v)
+    F, S, C = _fsc(q)
+    assert k.shape == q.shape == v.shape and k.dtype == q.dtype == v.dtype
+    locs = _locs(locs, S)
+    o = np.empty((F, locs.size, C))
+    rc = lib().oracle_dda(_ptr(q), _ptr(k), _ptr(v), _dt(q), F, S, C, head_dim, n_local, n_global, scale,
+                          _ptr(locs), locs.size, _ptr(o), nthreads)
+    if rc:
+        raise ValueError(f"oracle_dda rc={rc}")
+    return o
+
+
+def chain(x, w, G, eps=1e-5, head_dim=64, n_local=16, n_global=16, scale=0.0, locs=None, nthreads=0,
+          intermediates=False):
+    """GroupNorm -> conv3 -> dual-domain attention (Q = K = V), at sampled locations."""
+    x, w = _c(x), _c(w)
+    F, S, C = _fsc(x)
+    locs = _locs(locs, S)
+    out = np.empty((F, locs.size, C))
+    gn = np.empty_like(out) if intermediates else None
+    cv = np.empty_like(out) if intermediates else None
+    mean, rstd = np.empty(G), np.empty(G)
+    rc = lib().oracle_chain(_ptr(x), _ptr(w), _dt(x), F, S, C, G, eps, head_dim, n_local, n_global, scale,
+                            _ptr(locs), locs.size, _ptr(out), _ptr(gn), _ptr(cv), _ptr(mean), _ptr(rstd),
+                            nthreads)
+    if rc:
+        raise ValueError(f"oracle_chain rc={rc}")
+    if intermediates:
+        return out, gn, cv, mean, rstd
+    return out, mean, rstd
+
+
+def round_to(v: float, dt: int) -> float:
+    return lib().oracle_round_to(float(v), int(dt))

@@ -1,0 +1,394 @@
+/*
+ * CPU oracle of the Video-Infinity temporal module -- TEST INFRASTRUCTURE ONLY
+ * (see oracle.h for scope, layout and the passages each routine follows).
+ *
+ * Plain fp64 loops.  Threads only split independent work (voxel ranges for
+ * the GroupNorm sums, spatial locations for the conv and the attention);
+ * per-thread fp64 partial sums are combined in thread order.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---- helpers ---------------------------------------------------------- */
+
+static double load(const void* p, int dt, int64_t i) {
+    if (dt == 0) return (double)((const float*)p)[i];
+    uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+double oracle_round_to(double v, int dt) {
+    if (dt == 0) return (double)(float)v;
+    /* bf16 keeps 8 significant bits: v = m * 2^e with 0.5 <= |m| < 1, so the
+     * nearest bf16 is nearbyint(m * 2^8) * 2^(e-8) (ties to even under the
+     * default rounding mode).  Only the normal range is needed here. */
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e;
+    double m = frexp(v, &e);
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+static int resolve_threads(int nthreads) {
+    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    return nthreads;
+}
+
+typedef void (*range_fn)(void* ctx, int64_t begin, int64_t end, int tid);
+typedef struct {
+    range_fn fn;
+    void* ctx;
+    int64_t begin, end;
+    int tid;
+} range_job;
+
+static void* range_trampoline(void* p) {
+    range_job* j = (range_job*)p;
+    j->fn(j->ctx, j->begin, j->end, j->tid);
+    return NULL;
+}
+
+/* Split [0, n) into nthreads contiguous ranges; thread t gets range t. */
+static void parallel_ranges(int64_t n, int nthreads, range_fn fn, void* ctx) {
+    pthread_t th[256];
+    range_job jobs[256];
+    int made[256];
+    int64_t chunk = (n + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        int64_t b = chunk * t, e = b + chunk;
+        if (b > n) b = n;
+        if (e > n) e = n;
+        jobs[t] = (range_job){fn, ctx, b, e, t};
+        made[t] = t < nthreads - 1 && pthread_create(&th[t], NULL, range_trampoline, &jobs[t]) == 0;
+        if (!made[t]) fn(ctx, b, e, t);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (made[t]) pthread_join(th[t], NULL);
+}
+
+/* ---- GroupNorm with global statistics --------------------------------- */
+/* Group g owns the contiguous channels [g*C/G, (g+1)*C/G).  First pass: the
+ * mean of each group over every voxel of the whole video.  Second pass: the
+ * mean squared deviation from that global mean (population variance, divided
+ * by N_g).  eps is added inside the square root. */
+
+typedef struct {
+    const void* x;
+    int dt;
+    int64_t C, G, cg;
+    const double* mean; /* NULL in the first pass */
+    double* partial;    /* [nthreads][G] */
+} gn_ctx;
+
+static void gn_pass(void* vctx, int64_t r0, int64_t r1, int tid) {
+    gn_ctx* c = (gn_ctx*)vctx;
+    double* acc = c->partial + (int64_t)tid * c->G;
+    for (int64_t g = 0; g < c->G; ++g) acc[g] = 0.0;
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int64_t ch = 0; ch < c->C; ++ch) {
+            int64_t g = ch / c->cg;
+            double v = load(c->x, c->dt, r * c->C + ch);
+            if (c->mean) {
+                double d = v - c->mean[g];
+                acc[g] += d * d;
+            } else {
+                acc[g] += v;
+            }
+        }
+    }
+}
+
+int oracle_gn_stats(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, double eps,
+                    double* mean, double* var, double* rstd, int nthreads) {
+    if (!x || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || G < 1 || C % G) return 1;
+    nthreads = resolve_threads(nthreads);
+    int64_t rows = F * S, cg = C / G;
+    double n_g = (double)rows * (double)cg;
+    double* partial = (double*)calloc((size_t)nthreads * (size_t)G, sizeof(double));
+    double* mu = (double*)calloc((size_t)G, sizeof(double));
+    if (!partial || !mu) {
+        free(partial);
+        free(mu);
+        return 2;
+    }
+    gn_ctx c = {x, dt, C, G, cg, NULL, partial};
+    parallel_ranges(rows, nthreads, gn_pass, &c);
+    for (int64_t g = 0; g < G; ++g) {
+        double s = 0.0;
+        for (int t = 0; t < nthreads; ++t) s += partial[(int64_t)t * G + g];
+        mu[g] = s / n_g;
+    }
+    c.mean = mu;
+    parallel_ranges(rows, nthreads, gn_pass, &c);
+    for (int64_t g = 0; g < G; ++g) {
+        double s = 0.0;
+        for (int t = 0; t < nthreads; ++t) s += partial[(int64_t)t * G + g];
+        double v = s / n_g;
+        if (mean) mean[g] = mu[g];
+        if (var) var[g] = v;
+        if (rstd) rstd[g] = 1.0 / sqrt(v + eps);
+    }
+    free(partial);
+    free(mu);
+    return 0;
+}
+
+int oracle_groupnorm(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, double eps,
+                     const double* gamma, const double* beta, const int64_t* locs, int64_t n_locs,
+                     double* y, double* mean, double* rstd, int nthreads) {
+    if (!y || !locs || n_locs < 0) return 1;
+    double* mu = (double*)malloc(sizeof(double) * (size_t)G);
+    double* rs = (double*)malloc(sizeof(double) * (size_t)G);
+    if (!mu || !rs) {
+        free(mu);
+        free(rs);
+        return 2;
+    }
+    int rc = oracle_gn_stats(x, dt, F, S, C, G, eps, mu, NULL, rs, nthreads);
+    if (rc == 0) {
+        int64_t cg = C / G;
+        for (int64_t f = 0; f < F; ++f)
+            for (int64_t li = 0; li < n_locs; ++li) {
+                int64_t s = locs[li];
+                for (int64_t ch = 0; ch < C; ++ch) {
+                    int64_t g = ch / cg;
+                    double v = load(x, dt, (f * S + s) * C + ch);
+                    double o = (v - mu[g]) * rs[g];
+                    if (gamma) o *= gamma[ch];
+                    if (beta) o += beta[ch];
+                    y[(f * n_locs + li) * C + ch] = o;
+                }
+            }
+        for (int64_t g = 0; g < G; ++g) {
+            if (mean) mean[g] = mu[g];
+            if (rstd) rstd[g] = rs[g];
+        }
+    }
+    free(mu);
+    free(rs);
+    return rc;
+}
+
+/* ---- Temporal convolution, kernel 3, context padded ------------------- */
+/* The frame sequence of one spatial location is extended by one frame on each
+ * side (the receptive field of a kernel-3 convolution is one frame per side):
+ * the frame before the first is ctx_pre (zeros when absent, i.e. at the start
+ * of the whole video) and the frame after the last is ctx_post.  Tap k
+ * multiplies frame f+k-1 (cross-correlation order). */
+
+typedef struct {
+    const void *x, *pre, *post, *w;
+    const double* bias;
+    int dt;
+    int64_t F, S, C, n_locs;
+    const int64_t* locs;
+    double* y;
+} conv_ctx;
+
+static void conv_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
+    (void)tid;
+    conv_ctx* c = (conv_ctx*)vctx;
+    int64_t F = c->F, S = c->S, C = c->C;
+    double* col = (double*)malloc(sizeof(double) * (size_t)((F + 2) * C));
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(3 * C * C));
+    if (!col || !wd) abort();
+    for (int64_t i = 0; i < 3 * C * C; ++i) wd[i] = load(c->w, c->dt, i);
+    for (int64_t li = l0; li < l1; ++li) {
+        int64_t s = c->locs[li];
+        /* col[f+1] holds padded frame f, f = -1 .. F */
+        for (int64_t ch = 0; ch < C; ++ch) {
+            col[ch] = c->pre ? load(c->pre, c->dt, s * C + ch) : 0.0;
+            col[(F + 1) * C + ch] = c->post ? load(c->post, c->dt, s * C + ch) : 0.0;
+        }
+        for (int64_t f = 0; f < F; ++f)
+            for (int64_t ch = 0; ch < C; ++ch) col[(f + 1) * C + ch] = load(c->x, c->dt, (f * S + s) * C + ch);
+        for (int64_t f = 0; f < F; ++f)
+            for (int64_t co = 0; co < C; ++co) {
+                double acc = c->bias ? c->bias[co] : 0.0;
+                for (int64_t k = 0; k < 3; ++k) {
+                    const double* xr = col + (f + k) * C; /* padded frame (f + k - 1) */
+                    const double* wr = wd + (k * C + co) * C;
+                    for (int64_t ci = 0; ci < C; ++ci) acc += wr[ci] * xr[ci];
+                }
+                c->y[(f * c->n_locs + li) * C + co] = acc;
+            }
+    }
+    free(col);
+    free(wd);
+}
+
+int oracle_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* w,
+                 const double* bias, int dt, int64_t F, int64_t S, int64_t C, const int64_t* locs,
+                 int64_t n_locs, double* y, int nthreads) {
+    if (!x || !w || !y || !locs || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || n_locs < 0) return 1;
+    for (int64_t i = 0; i < n_locs; ++i)
+        if (locs[i] < 0 || locs[i] >= S) return 1;
+    nthreads = resolve_threads(nthreads);
+    if (nthreads > n_locs) nthreads = n_locs > 0 ? (int)n_locs : 1;
+    conv_ctx c = {x, ctx_pre, ctx_post, w, bias, dt, F, S, C, n_locs, locs, y};
+    parallel_ranges(n_locs, nthreads, conv_locs, &c);
+    return 0;
+}
+
+/* ---- Dual-domain attention -------------------------------------------- */
+/* Every query frame t attends over a key/value frame set that concatenates a
+ * local context (its neighbouring frames) and a global context (frames
+ * sampled uniformly over the whole video), each of size 16.  Readings:
+ *   local: min(L,F) consecutive frames starting at clamp(t - L/2, 0, F - L),
+ *          i.e. L/2 frames before t, t itself and L/2-1 after, shifted inward
+ *          at the ends of the video;
+ *   global: frames floor(i*F/Gk), i = 0..Gk-1;
+ *   the set is the concatenation of both lists (a multiset of min(L,F)+Gk
+ *   entries), so a frame in both lists carries two softmax terms;
+ *   scores are scale * q.k per head of head_dim contiguous channels, with no
+ *   bias or mask; softmax is exact (max-subtracted) in double. */
+
+int oracle_dda_keys(int64_t F, int64_t t, int n_local, int n_global, int64_t* keys) {
+    int64_t L = n_local, nl = L < F ? L : F;
+    int64_t hi = F - L > 0 ? F - L : 0;
+    int64_t st = t - L / 2;
+    if (st < 0) st = 0;
+    if (st > hi) st = hi;
+    int n = 0;
+    for (int64_t i = 0; i < nl; ++i) keys[n++] = st + i;
+    for (int64_t i = 0; i < n_global; ++i) keys[n++] = (i * F) / n_global;
+    return n;
+}
+
+typedef struct {
+    const void *q, *k, *v;
+    int dt;
+    int64_t F, S, C, n_locs;
+    int dh, L, Gk;
+    double scale;
+    const int64_t* locs;
+    double* o;
+} dda_ctx;
+
+static void dda_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
+    (void)tid;
+    dda_ctx* c = (dda_ctx*)vctx;
+    int64_t F = c->F, S = c->S, C = c->C;
+    int nmax = c->L + c->Gk;
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)nmax);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)nmax);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)c->dh);
+    if (!keys || !sc || !acc) abort();
+    for (int64_t li = l0; li < l1; ++li) {
+        int64_t s = c->locs[li];
+        for (int64_t h = 0; h < C / c->dh; ++h) {
+            int64_t c0 = h * c->dh;
+            for (int64_t t = 0; t < F; ++t) {
+                int n = oracle_dda_keys(F, t, c->L, c->Gk, keys);
+                double m = -INFINITY;
+                for (int j = 0; j < n; ++j) {
+                    double d = 0.0;
+                    for (int e = 0; e < c->dh; ++e)
+                        d += load(c->q, c->dt, (t * S + s) * C + c0 + e) *
+                             load(c->k, c->dt, (keys[j] * S + s) * C + c0 + e);
+                    sc[j] = c->scale * d;
+                    if (sc[j] > m) m = sc[j];
+                }
+                double den = 0.0;
+                for (int e = 0; e < c->dh; ++e) acc[e] = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    double p = exp(sc[j] - m);
+                    den += p;
+                    for (int e = 0; e < c->dh; ++e) acc[e] += p * load(c->v, c->dt, (keys[j] * S + s) * C + c0 + e);
+                }
+                for (int e = 0; e < c->dh; ++e) c->o[(t * c->n_locs + li) * C + c0 + e] = acc[e] / den;
+            }
+        }
+    }
+    free(keys);
+    free(sc);
+    free(acc);
+}
+
+int oracle_dda(const void* q, const void* k, const void* v, int dt, int64_t F, int64_t S, int64_t C,
+               int head_dim, int n_local, int n_global, double scale, const int64_t* locs,
+               int64_t n_locs, double* o, int nthreads) {
+    if (!q || !k || !v || !o || !locs || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || head_dim < 1 ||
+        C % head_dim || n_local < 0 || n_global < 0 || n_local + n_global < 1 || n_locs < 0)
+        return 1;
+    for (int64_t i = 0; i < n_locs; ++i)
+        if (locs[i] < 0 || locs[i] >= S) return 1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)head_dim);
+    nthreads = resolve_threads(nthreads);
+    if (nthreads > n_locs) nthreads = n_locs > 0 ? (int)n_locs : 1;
+    dda_ctx c = {q, k, v, dt, F, S, C, n_locs, head_dim, n_local, n_global, scale, locs, o};
+    parallel_ranges(n_locs, nthreads, dda_locs, &c);
+    return 0;
+}
+
+/* ---- The three modules in a row --------------------------------------- */
+/* Each module's output is a tensor of the I/O type, so intermediates are
+ * rounded to dt before they feed the next module.  The location subset stays
+ * exact: conv and attention never mix spatial locations, and the GroupNorm
+ * statistics are taken over the whole tensor. */
+
+int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int64_t C, int64_t G,
+                 double eps, int head_dim, int n_local, int n_global, double scale,
+                 const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
+                 double* mean, double* rstd, int nthreads) {
+    if (!out || !w || n_locs < 1) return 1;
+    size_t n = (size_t)(F * n_locs * C);
+    double* a = (double*)malloc(sizeof(double) * n);
+    double* b = (double*)malloc(sizeof(double) * n);
+    void* ta = malloc((dt == 0 ? 4 : 2) * n);
+    int64_t* seq = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_locs);
+    if (!a || !b || !ta || !seq) {
+        free(a);
+        free(b);
+        free(ta);
+        free(seq);
+        return 2;
+    }
+    int rc = oracle_groupnorm(x, dt, F, S, C, G, eps, NULL, NULL, locs, n_locs, a, mean, rstd, nthreads);
+    /* The sampled columns become a dense [F][n_locs][C] tensor in dt. */
+    for (int64_t i = 0; i < n_locs; ++i) seq[i] = i;
+    if (rc == 0) {
+        for (size_t i = 0; i < n; ++i) {
+            a[i] = oracle_round_to(a[i], dt);
+            if (dt == 0) {
+                ((float*)ta)[i] = (float)a[i];
+            } else {
+                float f = (float)a[i];
+                uint32_t u;
+                memcpy(&u, &f, 4);
+                ((uint16_t*)ta)[i] = (uint16_t)(u >> 16); /* exact: a[i] is a bf16 value */
+            }
+        }
+        if (gn_out) memcpy(gn_out, a, sizeof(double) * n);
+        rc = oracle_conv3(ta, NULL, NULL, w, NULL, dt, F, n_locs, C, seq, n_locs, b, nthreads);
+    }
+    if (rc == 0) {
+        for (size_t i = 0; i < n; ++i) {
+            b[i] = oracle_round_to(b[i], dt);
+            if (dt == 0) {
+                ((float*)ta)[i] = (float)b[i];
+            } else {
+                float f = (float)b[i];
+                uint32_t u;
+                memcpy(&u, &f, 4);
+                ((uint16_t*)ta)[i] = (uint16_t)(u >> 16);
+            }
+        }
+        if (conv_out) memcpy(conv_out, b, sizeof(double) * n);
+        rc = oracle_dda(ta, ta, ta, dt, F, n_locs, C, head_dim, n_local, n_global, scale, seq, n_locs, out,
+                        nthreads);
+    }
+    free(a);
+    free(b);
+    free(ta);
+    free(seq);
+    return rc;
+}

@@ -1,0 +1,84 @@
+/*
+ * CPU oracle of the Video-Infinity temporal module -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the bench's CPU-baseline leg may load
+ * this library.  It shares no code with the HIP path.  Every routine is the
+ * plain definition of what the temporal module computes, in fp64, following
+ * the write-up of "Video-Infinity: Distributed Long Video Generation" (page
+ * "新国立祭出视频生成“无限宝石“：2300帧仅需5分钟，提速100倍"):
+ *   - oracle_gn_stats / oracle_groupnorm: the GroupNorm-module paragraph
+ *     (group means first, aggregated to a global mean; then the standard
+ *     deviation computed with that global mean);
+ *   - oracle_conv3: the Conv-module paragraph (convolution along frames, the
+ *     sequence padded with the neighbouring clip's frames, n = receptive field);
+ *   - oracle_dda: the dual-domain attention paragraph and the paragraph that
+ *     sets both context sizes to 16 (local neighbour frames + frames sampled
+ *     uniformly over the whole video);
+ *   - oracle_chain: the three temporal modules in a row (the paragraph that
+ *     lists Attention, Conv and GroupNorm as the temporal modules).
+ * Readings of points the page leaves open are stated at each function.
+ *
+ * Tensors are dense channels-last [F][S][C] (S = H*W spatial locations), given
+ * as float32 (dt = 0) or bf16 bit patterns (dt = 1); inputs are widened
+ * exactly to double.  Outputs are double, for a list of spatial locations
+ * `locs` (n_locs entries), laid out [F][n_locs][C].  Temporal modules act on
+ * each spatial location independently, so a location subset is exact.
+ *
+ * Return value: 0 on success, nonzero on a bad argument.
+ * nthreads <= 0 uses every online core.
+ */
+#ifndef VINF_ORACLE_H
+#define VINF_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Global per-group statistics over all F*S voxels of the group's channels.
+ * mean[g] = sum x / N_g;  var[g] = sum (x - mean[g])^2 / N_g (biased);
+ * rstd[g] = 1 / sqrt(var[g] + eps).  Any of mean/var/rstd may be NULL. */
+int oracle_gn_stats(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, double eps,
+                    double* mean, double* var, double* rstd, int nthreads);
+
+/* y = (x - mean_g) * rstd_g * gamma_c + beta_c at the given locations.
+ * gamma/beta may be NULL (1 and 0).  mean/rstd outputs may be NULL. */
+int oracle_groupnorm(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, double eps,
+                     const double* gamma, const double* beta, const int64_t* locs, int64_t n_locs,
+                     double* y, double* mean, double* rstd, int nthreads);
+
+/* y[f,s,co] = bias[co] + sum_{k=0..2} sum_ci w[k][co][ci] * xt[f+k-1, s, ci],
+ * xt[-1] = ctx_pre (or 0 if NULL), xt[F] = ctx_post (or 0 if NULL).
+ * w is [3][C][C] in dt; ctx_* are [S][C] in dt; bias is [C] double or NULL. */
+int oracle_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* w,
+                 const double* bias, int dt, int64_t F, int64_t S, int64_t C, const int64_t* locs,
+                 int64_t n_locs, double* y, int nthreads);
+
+/* Key frames of query frame t: local frames st .. st+min(L,F)-1 with
+ * st = clamp(t - L/2, 0, max(F-L, 0)), then global frames floor(i*F/Gk),
+ * i = 0..Gk-1.  Writes min(L,F)+Gk frame indices to keys (a multiset: a frame
+ * in both lists appears twice).  Returns the count. */
+int oracle_dda_keys(int64_t F, int64_t t, int n_local, int n_global, int64_t* keys);
+
+/* o[t,s,h*dh+d] = sum_j e^{s_j - m} v[j,s,h*dh+d] / sum_j e^{s_j - m}, j over
+ * the key multiset of t, s_j = scale * q[t,s,h] . k[j,s,h], m = max_j s_j.
+ * Heads are contiguous head_dim-channel slices; C % head_dim == 0. */
+int oracle_dda(const void* q, const void* k, const void* v, int dt, int64_t F, int64_t S, int64_t C,
+               int head_dim, int n_local, int n_global, double scale, const int64_t* locs,
+               int64_t n_locs, double* o, int nthreads);
+
+/* GroupNorm (identity affine) -> round to dt -> conv3 (zero padded, no bias)
+ * -> round to dt -> dual-domain attention with Q = K = V = the conv output.
+ * gn_out / conv_out ([F][n_locs][C], rounded values) may be NULL. */
+int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int64_t C, int64_t G,
+                 double eps, int head_dim, int n_local, int n_global, double scale,
+                 const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
+                 double* mean, double* rstd, int nthreads);
+
+/* Round a double to the nearest value representable in dt (ties to even). */
+double oracle_round_to(double v, int dt);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
