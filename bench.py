@@ -1,0 +1,219 @@
+"""Throughput of the Video-Infinity temporal module on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole temporal module over one synthetic latent:
+GroupNorm with whole-video statistics -> kernel-3 temporal conv (zero pads at
+the video ends) -> dual-domain attention with Q = K = V = the conv output, at
+F=1024 frames, 64x40 locations, C=320 (5 heads of 64), bf16, 32 groups -- the
+VideoCrafter2 latent shape at 512x320.  Inputs and every intermediate live in
+HBM before the timed region starts; no allocation happens inside it.
+
+Prints ONE JSON line: voxels/s (F*H*W per step), per-module times, the
+roofline position of the dominant kernel (HIP events on the launch stream),
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+WORKLOAD = dict(name="m1024_chain_f1024_64x40x320_bf16", F=1024, H=64, W=40, C=320, G=32)
+SEED_CONFIG = 6  # seeds of the F=1024 64x40x320 workload in synth.CONFIGS
+
+# Which source file holds each kernel (for the traffic record's staleness check).
+KERNEL_SOURCES = {
+    "dda_bf16": "video_diffusion_temporal_amd/csrc/dual_domain_attn.hip",
+    "conv3_bf16": "video_diffusion_temporal_amd/csrc/temporal_conv3.hip",
+    "groupnorm": "video_diffusion_temporal_amd/csrc/groupnorm.hip",
+}
+
+
+def algorithmic_work(F, H, W, C, b=2):
+    """Bytes / flops each module must move or compute (the method's own work)."""
+    S = H * W
+    vox = F * S
+    return {
+        # read q, k, v once, write o; plus the 16 global K and V rows per location
+        "dda_bf16": dict(bound="hbm", bytes=vox * 4 * C * b + S * 32 * C * b, flops=vox * 128 * C),
+        # 6 C^2 flops per voxel (3 taps x C_in x C_out x 2)
+        "conv3_bf16": dict(bound="mfma", bytes=vox * 2 * C * b + 3 * C * C * b, flops=vox * 6 * C * C),
+        # two statistic sweeps + apply: 3 reads and 1 write
+        "groupnorm": dict(bound="hbm", bytes=vox * 4 * C * b, flops=vox * 8 * C),
+    }
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch from profiles/traffic_<kernel>.json, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, KERNEL_SOURCES[kernel])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(F, C, G, side=16):
+    """The oracle chain, as it stands, on F frames x side x side locations."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    H = W = side
+    x = synth.make_tensor(SEED_CONFIG, synth.X_GN, F, H, W, C, synth.BF16)
+    w = synth.make_conv_weight(SEED_CONFIG, C, synth.BF16)
+    threads = min(os.cpu_count() or 1, 16)
+    t = time.perf_counter()
+    oracle.chain(x, w, G, nthreads=threads)
+    dt = time.perf_counter() - t
+    vox = F * H * W
+    return {"value": vox / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle chain (GroupNorm stats+apply, conv3, attention) in fp64 on F={F}, "
+                      f"{H}x{W} locations, C={C}: {vox} voxels in {dt:.2f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--cpu-side", type=int, default=16, help="locations per side of the CPU-baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} requested)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import video_diffusion_temporal_amd as vinf
+
+    F, H, W, C, G = (WORKLOAD[k] for k in ("F", "H", "W", "C", "G"))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x_np = synth.make_tensor(SEED_CONFIG, synth.X_GN, F, H, W, C, synth.BF16)
+    w_np = synth.make_conv_weight(SEED_CONFIG, C, synth.BF16)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    wt = torch.from_numpy(w_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    g = torch.empty_like(x)
+    cv = torch.empty_like(x)
+    o = torch.empty_like(x)
+    mean = torch.empty(G, device=dev)
+    rstd = torch.empty(G, device=dev)
+    ws = torch.empty(vinf.groupnorm_workspace_bytes(F, H, W, C, G, x.dtype), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        vinf.groupnorm_global(x, G, out=g, mean_out=mean, rstd_out=rstd, workspace=ws, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        vinf.temporal_conv3(g, wt, out=cv, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        vinf.dual_domain_attn(cv, cv, cv, out=o, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mod_ms = {"groupnorm": 0.0, "conv3_bf16": 0.0, "dda_bf16": 0.0}
+    for e in evs:
+        mod_ms["groupnorm"] += e[0].elapsed_time(e[1])
+        mod_ms["conv3_bf16"] += e[1].elapsed_time(e[2])
+        mod_ms["dda_bf16"] += e[2].elapsed_time(e[3])
+    mod_ms = {k: v / args.steps for k, v in mod_ms.items()}
+    ms_step = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    vox = F * H * W
+
+    work = algorithmic_work(F, H, W, C)
+    kernels = {}
+    for k, ms in mod_ms.items():
+        wk = work[k]
+        gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+        tfl = wk["flops"] / (ms * 1e-3) / 1e12
+        kernels[k] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfl, 2),
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "frac_mfma_bf16": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4) if k == "conv3_bf16" else None}
+    # dominant single-launch kernel (the GroupNorm module is five launches)
+    dom = max(("conv3_bf16", "dda_bf16"), key=lambda k: mod_ms[k])
+    wk = work[dom]
+    if wk["bound"] == "hbm":
+        achieved = wk["bytes"] / (mod_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(dom)}
+    else:
+        achieved = wk["flops"] / (mod_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic_record(dom)}
+    roof["ms_per_launch"] = round(mod_ms[dom], 4)
+
+    parity = None
+    if not args.no_check:
+        import oracle
+
+        locs = np.array([0, 1337, H * W - 1], dtype=np.int64)
+        ref, _, _ = oracle.chain(x_np, w_np, G, locs=locs, nthreads=min(os.cpu_count() or 1, 16))
+        got = o.reshape(F, H * W, C)[:, torch.as_tensor(locs, device=dev)].float().cpu().numpy()
+        err = np.abs(got.astype(np.float64) - ref)
+        parity = {"locations": locs.tolist(), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                  "ok": bool(err.max() <= 2e-2 and err.mean() <= 2e-3)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(F, C, G, args.cpu_side)
+
+    out = {
+        "metric": "temporal-module voxels/sec (F*H'*W') at F=1024; % HBM peak, % MFMA peak",
+        "value": vox / (ms_step * 1e-3),
+        "unit": "voxels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latent, conv weights N(0,1/(3C)))",
+        "config": {"workload": WORKLOAD["name"], "F": F, "H": H, "W": W, "C": C, "heads": C // 64, "groups": G,
+                   "n_local": 16, "n_global": 16, "chain": "groupnorm->conv3->dual_domain_attn"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "wall_s_timed": wall,
+        "parity_sampled": parity,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

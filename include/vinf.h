@@ -1,0 +1,142 @@
+/*
+ * libvinf -- the temporal module of a video-diffusion layer, in the form
+ * Video-Infinity defines it, as hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * Source of the method: the write-up of "Video-Infinity: Distributed Long
+ * Video Generation" (page "新国立祭出视频生成“无限宝石“：2300帧仅需5分钟，提速100倍").
+ * Its temporal modules are Attention (dual-domain), Conv (temporal, with
+ * context) and GroupNorm (global statistics); each acts on the frames of
+ * every spatial location of a latent [F, H', W', C].  Here the whole video is
+ * one clip on one GPU.
+ *
+ * Conventions shared by every call
+ *   Layout     dense, contiguous, channels-last [F][H][W][C]; element
+ *              (f, h, w, c) at ((f*H + h)*W + w)*C + c.  No strides.
+ *   Types      vinf_dtype selects float32 or bfloat16 for the tensors named
+ *              "dt" below; gamma, beta, bias and statistics are float32.
+ *              bf16 results are rounded to nearest even from fp32.
+ *   Memory     every pointer is device memory owned by the caller; the
+ *              library allocates, frees and retains nothing.  Tensor
+ *              pointers (x, y, q, k, v, o, weight, ctx_*) must be 16-byte
+ *              aligned; float pointers 4-byte aligned.
+ *   Streams    `stream` is a hipStream_t (NULL: the null stream).  Calls only
+ *              enqueue work and return without synchronising.  The library
+ *              holds no state, so calls from several threads are safe.
+ *   Errors     arguments are checked on the host before anything is
+ *              enqueued; a rejected call returns VINF_ERR_INVALID_ARG or
+ *              VINF_ERR_UNSUPPORTED (or VINF_ERR_WORKSPACE) and has no
+ *              effect.  A failed launch returns VINF_ERR_HIP.  Faults during
+ *              execution surface at the caller's next synchronisation.
+ *              vinf_last_error() gives a message for the calling thread's
+ *              last failed call.  Nothing throws across this interface.
+ */
+#ifndef VINF_H
+#define VINF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VINF_OK = 0,
+    VINF_ERR_INVALID_ARG = 1, /* NULL / non-positive size / misaligned / aliasing / inconsistent */
+    VINF_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+    VINF_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    VINF_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} vinf_status;
+
+typedef enum { VINF_F32 = 0, VINF_BF16 = 1 } vinf_dtype;
+
+typedef void* vinf_stream; /* a hipStream_t */
+
+/*
+ * GroupNorm with statistics over the whole video (GroupNorm-module paragraph:
+ * group means first, aggregated to a global mean; then the standard deviation
+ * computed with that global mean, aggregated to a global standard deviation).
+ *
+ *   N_g     = F*H*W*C/groups voxel-channels of group g (channels
+ *             [g*C/groups, (g+1)*C/groups))
+ *   mean_g  = sum x / N_g                                   (pass 1)
+ *   var_g   = sum (x - mean_g)^2 / N_g                      (pass 2, biased)
+ *   y       = (x - mean_g) / sqrt(var_g + eps) * gamma_c + beta_c
+ *
+ * x, y      [F][H][W][C] in dt.  y == x (in place) is allowed; any other
+ *           overlap is rejected.
+ * gamma,beta  [C] float32 or NULL (1 and 0).
+ * mean_out, rstd_out  [groups] float32 or NULL; receive mean_g and
+ *           1/sqrt(var_g + eps).
+ * workspace device scratch of at least vinf_groupnorm_workspace_bytes(...)
+ *           bytes, 256-byte aligned; contents on entry do not matter.
+ * Limits    C % groups == 0; C % 8 == 0 (bf16) or C % 4 == 0 (f32);
+ *           C <= 8192; eps >= 0.
+ * The statistics are summed in a fixed order (per-block fp32 partials, then
+ * an fp64 combine), so results are bitwise reproducible run to run.
+ */
+size_t vinf_groupnorm_workspace_bytes(int F, int H, int W, int C, int groups, vinf_dtype dt);
+vinf_status vinf_groupnorm_global(const void* x, void* y, const float* gamma, const float* beta,
+                                  float* mean_out, float* rstd_out, int F, int H, int W, int C,
+                                  int groups, float eps, vinf_dtype dt, void* workspace,
+                                  size_t workspace_bytes, vinf_stream stream);
+
+/*
+ * Temporal convolution, kernel 3, with context padding (Conv-module
+ * paragraph: convolution along the frame axis of each spatial location; the
+ * clip is padded with the last frames of the previous clip and the first
+ * frames of the next one, as many as the receptive field -- one per side for
+ * kernel 3).
+ *
+ *   y[f,h,w,co] = bias[co] + sum_{k=0..2} sum_ci weight[k][co][ci] * xt[f+k-1,h,w,ci]
+ *   xt[-1] = ctx_pre, xt[F] = ctx_post (zeros when NULL: the ends of the video)
+ *
+ * x, y      [F][H][W][C] in dt; y must not overlap x, weight or ctx_*.
+ * ctx_pre, ctx_post  [H][W][C] in dt, or NULL.
+ * weight    [3][C_out=C][C_in=C] in dt (tap k multiplies frame f+k-1; a torch
+ *           Conv1d weight [C_out][C_in][3] maps to it by permute(2,0,1)).
+ * bias      [C] float32 or NULL.
+ * Limits    bf16: C % 32 == 0 (bf16 MFMA tiles); f32: C % 4 == 0.
+ */
+vinf_status vinf_temporal_conv3(const void* x, const void* ctx_pre, const void* ctx_post,
+                                const void* weight, const float* bias, void* y, int F, int H, int W,
+                                int C, vinf_dtype dt, vinf_stream stream);
+
+/*
+ * Dual-domain temporal attention (dual-domain attention paragraph, and the
+ * paragraph that sets both context sizes to 16): at each spatial location and
+ * head, query frame t attends over the concatenation of a local context and a
+ * global context.
+ *
+ *   local(t)  = frames st .. st+min(n_local,F)-1,
+ *               st = clamp(t - n_local/2, 0, max(F - n_local, 0))
+ *               (centred on t, shifted inward at the ends of the video)
+ *   global    = frames floor(i*F/n_global), i = 0..n_global-1
+ *   J(t)      = local(t) ++ global   (a multiset: a frame in both counts twice)
+ *   o[t]      = sum_{j in J(t)} e^{s_j} v[j] / sum_{j in J(t)} e^{s_j},
+ *   s_j       = scale * q[t] . k[j]  over the head's head_dim channels
+ *
+ * q, k, v   [F][H][W][C] in dt, already projected; head h owns channels
+ *           [h*head_dim, (h+1)*head_dim).
+ * o         [F][H][W][C] in dt, before any output projection; must not
+ *           overlap q, k or v.
+ * scale     <= 0 selects 1/sqrt(head_dim).
+ * Limits    head_dim == 64, C % 64 == 0, n_local == 16 and n_global == 16
+ *           (anything else: VINF_ERR_UNSUPPORTED).  F >= 1 (F < 16 uses all
+ *           F frames as the local context).
+ */
+vinf_status vinf_dual_domain_attn(const void* q, const void* k, const void* v, void* o, int F, int H,
+                                  int W, int C, int head_dim, int n_local, int n_global, float scale,
+                                  vinf_dtype dt, vinf_stream stream);
+
+/* Static description of a status code. */
+const char* vinf_status_string(vinf_status s);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* vinf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VINF_H */

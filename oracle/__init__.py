@@ -44,7 +44,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_conv3.argtypes = [vp, vp, vp, vp, vp, i, i64, i64, i64, vp, i64, vp, i]
         L.oracle_dda_keys.argtypes = [i64, i64, i, i, vp]
         L.oracle_dda.argtypes = [vp, vp, vp, i, i64, i64, i64, i, i, i, d, vp, i64, vp, i]
-        L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, vp, i64, vp, vp, vp, vp, vp, i]
+        L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, vp, i64, vp, vp, vp, vp, vp, vp, vp, i]
         L.oracle_round_to.argtypes = [d, i]
         L.oracle_round_to.restype = d
         for fn in ("oracle_gn_stats", "oracle_groupnorm", "oracle_conv3", "oracle_dda_keys", "oracle_dda",
@@ -149,20 +149,30 @@ def dda(q, k, v, head_dim=64, n_local=16, n_global=16, scale=0.0, locs=None, nth
 
 
 def chain(x, w, G, eps=1e-5, head_dim=64, n_local=16, n_global=16, scale=0.0, locs=None, nthreads=0,
-          intermediates=False):
-    """GroupNorm -> conv3 -> dual-domain attention (Q = K = V), at sampled locations."""
+          intermediates=False, exact=False):
+    """GroupNorm -> conv3 -> dual-domain attention (Q = K = V), at sampled locations.
+
+    Returns (out, mean, rstd); with intermediates=True (out, gn, conv, mean,
+    rstd) where gn and conv are the rounded intermediates; with exact=True
+    also (gn_exact, conv_exact), the intermediates before rounding.
+    """
     x, w = _c(x), _c(w)
     F, S, C = _fsc(x)
     locs = _locs(locs, S)
     out = np.empty((F, locs.size, C))
-    gn = np.empty_like(out) if intermediates else None
-    cv = np.empty_like(out) if intermediates else None
+    want = intermediates or exact
+    gn = np.empty_like(out) if want else None
+    cv = np.empty_like(out) if want else None
+    gx = np.empty_like(out) if exact else None
+    cx = np.empty_like(out) if exact else None
     mean, rstd = np.empty(G), np.empty(G)
     rc = lib().oracle_chain(_ptr(x), _ptr(w), _dt(x), F, S, C, G, eps, head_dim, n_local, n_global, scale,
-                            _ptr(locs), locs.size, _ptr(out), _ptr(gn), _ptr(cv), _ptr(mean), _ptr(rstd),
-                            nthreads)
+                            _ptr(locs), locs.size, _ptr(out), _ptr(gn), _ptr(cv), _ptr(gx), _ptr(cx), _ptr(mean),
+                            _ptr(rstd), nthreads)
     if rc:
         raise ValueError(f"oracle_chain rc={rc}")
+    if exact:
+        return out, gn, cv, gx, cx, mean, rstd
     if intermediates:
         return out, gn, cv, mean, rstd
     return out, mean, rstd

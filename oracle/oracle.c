@@ -36,7 +36,10 @@ double oracle_round_to(double v, int dt) {
 }
 
 static int resolve_threads(int nthreads) {
-    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads <= 0) { /* default: every online core, at most 16 */
+        nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+        if (nthreads > 16) nthreads = 16;
+    }
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     return nthreads;
@@ -338,7 +341,7 @@ int oracle_dda(const void* q, const void* k, const void* v, int dt, int64_t F, i
 int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int64_t C, int64_t G,
                  double eps, int head_dim, int n_local, int n_global, double scale,
                  const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
-                 double* mean, double* rstd, int nthreads) {
+                 double* gn_exact, double* conv_exact, double* mean, double* rstd, int nthreads) {
     if (!out || !w || n_locs < 1) return 1;
     size_t n = (size_t)(F * n_locs * C);
     double* a = (double*)malloc(sizeof(double) * n);
@@ -356,6 +359,7 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
     /* The sampled columns become a dense [F][n_locs][C] tensor in dt. */
     for (int64_t i = 0; i < n_locs; ++i) seq[i] = i;
     if (rc == 0) {
+        if (gn_exact) memcpy(gn_exact, a, sizeof(double) * n);
         for (size_t i = 0; i < n; ++i) {
             a[i] = oracle_round_to(a[i], dt);
             if (dt == 0) {
@@ -371,6 +375,7 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
         rc = oracle_conv3(ta, NULL, NULL, w, NULL, dt, F, n_locs, C, seq, n_locs, b, nthreads);
     }
     if (rc == 0) {
+        if (conv_exact) memcpy(conv_exact, b, sizeof(double) * n);
         for (size_t i = 0; i < n; ++i) {
             b[i] = oracle_round_to(b[i], dt);
             if (dt == 0) {

@@ -25,7 +25,7 @@
  * each spatial location independently, so a location subset is exact.
  *
  * Return value: 0 on success, nonzero on a bad argument.
- * nthreads <= 0 uses every online core.
+ * nthreads <= 0 uses every online core, at most 16.
  */
 #ifndef VINF_ORACLE_H
 #define VINF_ORACLE_H
@@ -69,11 +69,12 @@ int oracle_dda(const void* q, const void* k, const void* v, int dt, int64_t F, i
 
 /* GroupNorm (identity affine) -> round to dt -> conv3 (zero padded, no bias)
  * -> round to dt -> dual-domain attention with Q = K = V = the conv output.
- * gn_out / conv_out ([F][n_locs][C], rounded values) may be NULL. */
+ * gn_out / conv_out ([F][n_locs][C], rounded values) and gn_exact /
+ * conv_exact (the same before rounding) may be NULL. */
 int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int64_t C, int64_t G,
                  double eps, int head_dim, int n_local, int n_global, double scale,
                  const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
-                 double* mean, double* rstd, int nthreads);
+                 double* gn_exact, double* conv_exact, double* mean, double* rstd, int nthreads);
 
 /* Round a double to the nearest value representable in dt (ties to even). */
 double oracle_round_to(double v, int dt);

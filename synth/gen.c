@@ -73,11 +73,14 @@ static void* worker(void* p) {
     return NULL;
 }
 
-/* Fill out[0..n) (float or bf16 bits).  nthreads <= 0 uses every online core. */
+/* Fill out[0..n) (float or bf16 bits).  nthreads <= 0 uses every online core, at most 16. */
 int synth_normal(void* out, uint64_t n, int dtype, uint64_t seed, double scale, uint64_t frame_elems,
                  double frame_slope, int nthreads) {
     if (!out || (dtype != 0 && dtype != 1)) return 1;
-    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads <= 0) { /* default: every online core, at most 16 */
+        nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+        if (nthreads > 16) nthreads = 16;
+    }
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if ((uint64_t)nthreads > n / 65536 + 1) nthreads = (int)(n / 65536 + 1);

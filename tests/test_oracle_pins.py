@@ -361,6 +361,10 @@ def test_chain_composes_the_three_modules():
     locs = [5, 1]
     out_s, _, _ = oracle.chain(x, w, G, locs=locs)
     assert np.array_equal(out_s, out[:, locs])
+    # the exact (pre-rounding) intermediates
+    _, gn2, cv2, gx, cx, _, _ = oracle.chain(x, w, G, exact=True)
+    assert np.array_equal(gx, y) and np.array_equal(gn2, gn) and np.array_equal(cv2, cv)
+    assert np.array_equal(cx, oracle.conv3(bits, w))
 
 
 def test_round_to_bf16_matches_torch():

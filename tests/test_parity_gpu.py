@@ -1,0 +1,338 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small shapes compare every output element and span several workgroup tiles
+with ragged tails; the full workloads compare sampled spatial locations (the
+oracle computes those columns exactly: conv and attention never mix
+locations, and the GroupNorm statistics are compared as well).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import video_diffusion_temporal_amd as vinf
+from helpers import TOL, announce, bits, check, check_stats, fetch, sample_locs, upload
+
+pytestmark = pytest.mark.gpu
+
+BF, FP = synth.BF16, synth.F32
+
+
+def rnd(shape, seed, dt, scale=1.0):
+    return synth.normal(int(np.prod(shape)), seed, dt, scale).reshape(shape)
+
+
+# ------------------------------------------------------------------ GroupNorm
+
+@pytest.mark.parametrize("F,H,W,C,G,dt", [
+    (16, 8, 5, 64, 8, FP),          # the tiny float32 workload
+    (37, 7, 9, 320, 32, BF),        # ragged rows, C/G = 10
+    (5, 3, 3, 640, 32, BF),
+    (3, 1, 1, 1280, 32, BF),        # fewer rows than one block's row slots
+    (1, 1, 1, 8, 1, BF),            # a single voxel row
+    (9, 4, 4, 2048, 16, BF),        # 256 vectors per row
+    (2, 3, 2, 4096, 8, BF),         # 512 vectors per row (one row slot per block)
+    (11, 5, 3, 12, 3, FP),          # C/G = 4
+])
+def test_groupnorm_small(F, H, W, C, G, dt):
+    announce(f"groupnorm F={F} H={H} W={W} C={C} G={G} dt={dt}")
+    x = rnd((F, H, W, C), 1000 + C + F, dt)
+    # |y| stays below 8, where one bf16 half-ulp (2^-6) is under the 2e-2 bar
+    gamma = np.linspace(0.5, 1.25, C).astype(np.float32)
+    beta = np.linspace(-0.5, 0.5, C).astype(np.float32)
+    y, mean, rstd = vinf.groupnorm_global(upload(x), G, 1e-5, torch.from_numpy(gamma).cuda(),
+                                          torch.from_numpy(beta).cuda())
+    ref, rm, rr = oracle.groupnorm(x, G, 1e-5, gamma.astype(np.float64), beta.astype(np.float64))
+    check(fetch(y), ref, dt, "y")
+    check_stats(mean, rstd, rm, rr, "stats")
+
+
+def test_groupnorm_in_place_and_deterministic():
+    F, H, W, C, G = 33, 6, 6, 320, 32
+    x = rnd((F, H, W, C), 77, BF)
+    xd = upload(x)
+    y1, m1, r1 = vinf.groupnorm_global(xd, G)
+    y2, m2, r2 = vinf.groupnorm_global(xd, G)
+    assert np.array_equal(bits(y1), bits(y2)) and torch.equal(m1, m2) and torch.equal(r1, r2)
+    xi = xd.clone()
+    y3, _, _ = vinf.groupnorm_global(xi, G, out=xi)
+    assert y3.data_ptr() == xi.data_ptr()
+    assert np.array_equal(bits(xi), bits(y1))
+
+
+def test_groupnorm_drifting_mean():
+    # Per-frame offset 0.3 t/F: the global mean is far from zero relative to
+    # the per-voxel noise in late frames; two passes keep the variance exact.
+    F, H, W, C, G = 2300, 2, 2, 64, 8
+    x = synth.make_tensor(9, synth.X_GN, F, H, W, C, BF, slope=0.3)
+    y, mean, rstd = vinf.groupnorm_global(upload(x), G)
+    ref, rm, rr = oracle.groupnorm(x, G)
+    check(fetch(y), ref, BF, "y")
+    check_stats(mean, rstd, rm, rr, "stats")
+
+
+# ------------------------------------------------------------- temporal conv
+
+@pytest.mark.parametrize("F,H,W,C,dt,ctx,bias", [
+    (16, 8, 5, 64, FP, False, False),     # the tiny float32 workload
+    (37, 7, 9, 320, BF, False, False),    # ragged frame (8) and location (16) tiles, 2 N tiles of 160
+    (19, 3, 7, 320, BF, True, True),
+    (9, 5, 5, 128, BF, True, False),      # N tile 128
+    (10, 4, 5, 64, BF, False, True),      # N tile 64
+    (7, 3, 3, 96, BF, True, True),        # N tile 32
+    (1, 4, 4, 640, BF, True, False),      # a single frame: both pads used
+    (2, 1, 1, 1280, BF, False, False),
+    (13, 2, 3, 40, FP, True, True),
+])
+def test_conv_small(F, H, W, C, dt, ctx, bias):
+    announce(f"conv F={F} H={H} W={W} C={C} dt={dt} ctx={ctx} bias={bias}")
+    x = rnd((F, H, W, C), 2000 + C + F, dt)
+    w = rnd((3, C, C), 2100 + C, dt, 1 / math.sqrt(3 * C))
+    pre = rnd((H, W, C), 2200 + C, dt) if ctx else None
+    post = rnd((H, W, C), 2300 + C, dt) if ctx else None
+    b = np.linspace(-0.3, 0.3, C).astype(np.float32) if bias else None
+    y = vinf.temporal_conv3(upload(x), upload(w), None if pre is None else upload(pre),
+                            None if post is None else upload(post), None if b is None else torch.from_numpy(b).cuda())
+    ref = oracle.conv3(x, w, pre, post, None if b is None else b.astype(np.float64))
+    check(fetch(y), ref, dt, "y")
+
+
+def bf16_eye_taps(C, tap):
+    w = np.zeros((3, C, C), np.float32)
+    w[tap] = np.eye(C, dtype=np.float32)
+    return (w.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_conv_identity_and_shift_bitwise():
+    F, H, W, C = 21, 5, 7, 320
+    x = rnd((F, H, W, C), 31, BF)
+    pre, post = rnd((H, W, C), 32, BF), rnd((H, W, C), 33, BF)
+    xd, pd, qd = upload(x), upload(pre), upload(post)
+    y = vinf.temporal_conv3(xd, upload(bf16_eye_taps(C, 1)), pd, qd)
+    assert np.array_equal(bits(y), x)
+    y = vinf.temporal_conv3(xd, upload(bf16_eye_taps(C, 0)), pd, qd)   # y[f] = x[f-1], y[0] = ctx_pre
+    yb = bits(y)
+    assert np.array_equal(yb[1:], x[:-1]) and np.array_equal(yb[0], pre)
+    y = vinf.temporal_conv3(xd, upload(bf16_eye_taps(C, 2)))           # y[f] = x[f+1], zero after the end
+    yb = bits(y)
+    assert np.array_equal(yb[:-1], x[1:]) and not yb[-1].any()
+
+
+def test_conv_clip_split_equals_whole_bitwise():
+    # The clip-parallel view on one GPU: each clip padded with its neighbours'
+    # edge frames reproduces the whole-video result exactly.
+    F, H, W, C = 40, 4, 6, 320
+    x = rnd((F, H, W, C), 41, BF)
+    w = rnd((3, C, C), 42, BF, 1 / math.sqrt(3 * C))
+    xd, wd = upload(x), upload(w)
+    whole = bits(vinf.temporal_conv3(xd, wd))
+    for a, b in [(0, 13), (13, 29), (29, 40)]:
+        pre = xd[a - 1].contiguous() if a > 0 else None
+        post = xd[b].contiguous() if b < F else None
+        part = vinf.temporal_conv3(xd[a:b].contiguous(), wd, pre, post)
+        assert np.array_equal(bits(part), whole[a:b])
+
+
+def test_conv_deterministic():
+    F, H, W, C = 17, 6, 6, 640
+    x, w = upload(rnd((F, H, W, C), 51, BF)), upload(rnd((3, C, C), 52, BF, 0.02))
+    assert np.array_equal(bits(vinf.temporal_conv3(x, w)), bits(vinf.temporal_conv3(x, w)))
+
+
+# --------------------------------------------------- dual-domain attention
+
+@pytest.mark.parametrize("F,H,W,C,dt", [
+    (16, 8, 5, 64, FP),      # the tiny float32 workload
+    (1, 2, 3, 64, BF),
+    (5, 3, 2, 128, BF),      # F < 16: local context = all frames, repeated global frames
+    (16, 4, 4, 320, BF),
+    (17, 3, 3, 64, BF),
+    (40, 2, 5, 192, BF),
+    (300, 2, 2, 320, BF),    # two query blocks of 256, ragged second block
+    (513, 1, 3, 128, BF),    # three blocks, one query in the last
+    (70, 3, 1, 128, FP),
+])
+def test_attention_small(F, H, W, C, dt):
+    announce(f"attention F={F} H={H} W={W} C={C} dt={dt}")
+    q, k, v = (rnd((F, H, W, C), 3000 + 10 * i + F, dt) for i in range(3))
+    o = vinf.dual_domain_attn(upload(q), upload(k), upload(v))
+    check(fetch(o), oracle.dda(q, k, v), dt, "o")
+
+
+def test_attention_closed_forms_on_gpu():
+    F, H, W, C = 200, 2, 3, 128
+    q, v = rnd((F, H, W, C), 61, BF), rnd((F, H, W, C), 62, BF)
+    kc = np.broadcast_to(rnd((1, H, W, C), 63, BF), (F, H, W, C)).copy()
+    o = fetch(vinf.dual_domain_attn(upload(q), upload(kc), upload(v)))
+    vf = synth.bf16_bits_to_f32(v).reshape(F, H * W, C).astype(np.float64)
+    for t in (0, 7, 8, 9, 100, 191, 192, 199):
+        keys = oracle.dda_keys(F, t)
+        check(o[t:t + 1], vf[keys].mean(axis=0, keepdims=True), BF, f"constant-K mean of V, t={t}")
+    vc = np.broadcast_to(v[:1], v.shape).copy()
+    o = fetch(vinf.dual_domain_attn(upload(q), upload(kc), upload(vc)))
+    check(o, np.broadcast_to(vf[:1], o.shape), BF, "constant V")
+
+
+def test_attention_scale_and_determinism():
+    F, H, W, C = 64, 2, 2, 128
+    q, k, v = (upload(rnd((F, H, W, C), 70 + i, BF)) for i in range(3))
+    o1 = vinf.dual_domain_attn(q, k, v)
+    o2 = vinf.dual_domain_attn(q, k, v, scale=0.125)
+    assert np.array_equal(bits(o1), bits(o2))
+    o3 = vinf.dual_domain_attn(q, k, v, scale=0.05)
+    ref = oracle.dda(*(bits(t) for t in (q, k, v)), scale=0.05)
+    check(fetch(o3), ref, BF, "scale 0.05")
+
+
+# ------------------------------------------------------------- full workloads
+
+CFG = synth.CONFIGS
+
+
+def run_modules(cfgno):
+    """Every module on its own seeded inputs at full size, sampled locations checked."""
+    c = CFG[cfgno]
+    F, H, W, C, G, dt = c["F"], c["H"], c["W"], c["C"], c["G"], c["dtype"]
+    S = H * W
+    locs = sample_locs(S, 8, seed=cfgno)
+    announce(f"{c['name']}: groupnorm")
+    x = synth.make_tensor(cfgno, synth.X_GN, F, H, W, C, dt, c["slope"])
+    y, mean, rstd = vinf.groupnorm_global(upload(x), G)
+    ref, rm, rr = oracle.groupnorm(x, G, locs=locs)
+    check(fetch(y, locs), ref, dt, "groupnorm")
+    check_stats(mean, rstd, rm, rr, "groupnorm stats")
+    del x, y
+    announce(f"{c['name']}: temporal conv")
+    x = synth.make_tensor(cfgno, synth.X_CONV, F, H, W, C, dt, c["slope"])
+    w = synth.make_conv_weight(cfgno, C, dt)
+    y = vinf.temporal_conv3(upload(x), upload(w))
+    check(fetch(y, locs), oracle.conv3(x, w, locs=locs), dt, "conv3")
+    del x, y
+    announce(f"{c['name']}: dual-domain attention")
+    q, k, v = (synth.make_tensor(cfgno, tid, F, H, W, C, dt, c["slope"]) for tid in (synth.Q, synth.K, synth.V))
+    o = vinf.dual_domain_attn(upload(q), upload(k), upload(v))
+    check(fetch(o, locs), oracle.dda(q, k, v, locs=locs), dt, "attention")
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float64 values that are exactly bf16 -> uint16 bits."""
+    return (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_step(r: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """The bf16 neighbour of bf16 values r in direction d (+1 up, -1 down)."""
+    b = to_bf16_bits(r).astype(np.int64)
+    key = np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF) + d
+    nb = np.where(key >= 0, key, 0x8000 | (-key)).astype(np.uint32)
+    return (nb << 16).view(np.float32).astype(np.float64)
+
+
+def rounding_alternatives(exact: np.ndarray, rounded: np.ndarray, frac: float = 2.0 ** -10):
+    """Where `exact` lies within frac*ulp of the midpoint between `rounded` and
+    its neighbour on exact's side, both are correct roundings of a value the
+    kernel accumulates in fp32.  Returns (ambiguous mask, other rounding)."""
+    d = np.where(exact >= rounded, 1, -1)
+    alt = bf16_step(rounded, d)
+    amb = np.abs(exact - 0.5 * (rounded + alt)) <= frac * np.abs(alt - rounded)
+    return amb & (exact != rounded), alt
+
+
+def run_chain(cfgno):
+    """GroupNorm -> conv3 -> attention with Q = K = V.
+
+    Each module's output is a bf16 tensor, so both sides round the two
+    intermediates; an intermediate whose exact value sits within fp32
+    accumulation error of a rounding midpoint has two correct roundings.  The
+    test checks (1) every stage of the full-size GPU chain at the bar, (2) the
+    GPU conv and attention on the oracle's own rounded intermediates at the
+    bar, (3) that the GPU intermediates differ from the oracle's only at such
+    ambiguous elements, and only by the other rounding, and (4) every final
+    output at the bar, except that an output above it must depend on an
+    ambiguous intermediate and meet the bar for some valid choice of those
+    roundings (recomputed by the oracle)."""
+    c = CFG[cfgno]
+    F, H, W, C, G, dt = c["F"], c["H"], c["W"], c["C"], c["G"], c["dtype"]
+    S = H * W
+    locs = sample_locs(S, 8, seed=cfgno)
+    nl = locs.size
+    announce(f"{c['name']}: chain groupnorm -> conv3 -> attention")
+    x = synth.make_tensor(cfgno, synth.X_GN, F, H, W, C, dt)
+    w = synth.make_conv_weight(cfgno, C, dt)
+    xd, wd = upload(x), upload(w)
+    g, mean, rstd = vinf.groupnorm_global(xd, G)
+    del xd
+    cv = vinf.temporal_conv3(g, wd)
+    gs = fetch(g, locs)
+    del g
+    o = vinf.dual_domain_attn(cv, cv, cv)
+    cs, os_ = fetch(cv, locs), fetch(o, locs)
+    del cv, o
+    out, gn_r, cv_r, gn_x, cv_x, rm, rr = oracle.chain(x, w, G, locs=locs, exact=True)
+    del x
+    check_stats(mean, rstd, rm, rr, "chain groupnorm stats")
+
+    # (1) stages against the exact oracle values
+    check(gs, gn_x, dt, "chain groupnorm")
+    check(cs, cv_x, dt, "chain conv3")
+
+    # (2) GPU conv / attention on the oracle's rounded intermediates
+    gcol = upload(to_bf16_bits(gn_r).reshape(F, 1, nl, C))
+    check(fetch(vinf.temporal_conv3(gcol, wd)), oracle.conv3(to_bf16_bits(gn_r), w), dt, "conv3 on oracle input")
+    ccol = upload(to_bf16_bits(cv_r).reshape(F, 1, nl, C))
+    check(fetch(vinf.dual_domain_attn(ccol, ccol, ccol)), out, dt, "attention on oracle input")
+    del gcol, ccol
+
+    # (3) intermediates differ only by the other correct rounding
+    g_amb, g_alt = rounding_alternatives(gn_x, gn_r)
+    gdiff = gs != gn_r
+    assert np.all(g_amb[gdiff]) and np.array_equal(gs[gdiff], g_alt[gdiff]), "groupnorm rounding outside ties"
+    c_amb, c_alt = rounding_alternatives(cv_x, cv_r)
+    flagged = c_amb.copy()
+    for f, li in set(zip(*np.nonzero(gdiff.any(axis=2)))):   # a groupnorm tie moves nearby conv outputs
+        flagged[max(f - 1, 0):f + 2, li, :] = True
+    cdiff = cs != cv_r
+    assert np.all(flagged[cdiff]), "conv3 rounding differs away from ties"
+    announce(f"  intermediate ties taken the other way: groupnorm {int(gdiff.sum())}, conv3 {int(cdiff.sum())} "
+             f"(ambiguous {int(c_amb.sum())} of {c_amb.size})")
+
+    # (4) final outputs
+    max_tol, mean_tol = TOL[dt]
+    err = np.abs(os_ - out)
+    assert err.mean() <= mean_tol, f"chain attention mean-abs {err.mean():.3e}"
+    bad = np.argwhere(err > max_tol)
+    announce(f"  chain attention: max-abs {err.max():.3e} mean-abs {err.mean():.3e}, "
+             f"{len(bad)} elements above {max_tol} to resolve")
+    resolved = set()
+    for t, li, ch in bad:
+        h = ch // 64
+        if (t, li, h) in resolved:
+            continue
+        frames = sorted(set([int(t)] + [int(j) for j in oracle.dda_keys(F, int(t))]))
+        cand = [(fr, cc) for fr in frames for cc in range(64 * h, 64 * h + 64) if c_amb[fr, li, cc]]
+        assert 0 < len(cand) <= 8, f"output ({t},{li},{ch}) above the bar with {len(cand)} ambiguous inputs"
+        ok = False
+        for mask in range(1, 1 << len(cand)):
+            col = cv_r[:, li, :].copy()
+            for b, (fr, cc) in enumerate(cand):
+                if mask >> b & 1:
+                    col[fr, cc] = c_alt[fr, li, cc]
+            cb = to_bf16_bits(col).reshape(F, 1, C)
+            alt = oracle.dda(cb, cb, cb)[t, 0, 64 * h:64 * h + 64]
+            if np.abs(os_[t, li, 64 * h:64 * h + 64] - alt).max() <= max_tol:
+                ok = True
+                break
+        assert ok, f"output ({t},{li},{ch}) meets the bar under no valid rounding of its inputs"
+        resolved.add((t, li, h))
+
+
+@pytest.mark.parametrize("cfgno", [1, 2, 3, 4])
+def test_workload_modules(cfgno):
+    run_modules(cfgno)
+
+
+@pytest.mark.parametrize("cfgno", [5, 6])
+def test_workload_chain(cfgno):
+    run_chain(cfgno)

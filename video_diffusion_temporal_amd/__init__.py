@@ -1,0 +1,162 @@
+"""Python binding of libvinf (the Video-Infinity temporal module on gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libvinf.so.  PyTorch supplies device memory and the current stream.
+Call names match the C ABI in include/vinf.h:
+
+    groupnorm_global(x, groups, eps=1e-5, ...)      -> (y, mean, rstd)
+    temporal_conv3(x, weight, ctx_pre=None, ...)     -> y
+    dual_domain_attn(q, k, v, ...)                   -> o
+
+Tensors are CUDA (HIP) tensors, contiguous, channels-last [F, H, W, C],
+float32 or bfloat16.  There is no CPU fallback: without the built library
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["groupnorm_global", "groupnorm_workspace_bytes", "temporal_conv3", "dual_domain_attn", "VinfError",
+           "library_path", "load", "VINF_F32", "VINF_BF16"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libvinf.so")
+
+VINF_OK, VINF_ERR_INVALID_ARG, VINF_ERR_UNSUPPORTED, VINF_ERR_WORKSPACE, VINF_ERR_HIP = range(5)
+VINF_F32, VINF_BF16 = 0, 1
+
+_lib = None
+
+
+class VinfError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libvinf.so (built by video_diffusion_temporal_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built; run `python -m video_diffusion_temporal_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.vinf_groupnorm_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.vinf_groupnorm_workspace_bytes.restype = sz
+        L.vinf_groupnorm_global.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        L.vinf_temporal_conv3.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.vinf_dual_domain_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+        for fn in ("vinf_groupnorm_global", "vinf_temporal_conv3", "vinf_dual_domain_attn"):
+            getattr(L, fn).restype = ctypes.c_int
+        L.vinf_status_string.argtypes = [i]
+        L.vinf_status_string.restype = ctypes.c_char_p
+        L.vinf_last_error.argtypes = []
+        L.vinf_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != VINF_OK:
+        raise VinfError(fn, status, load().vinf_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return VINF_BF16
+    if t.dtype == torch.float32:
+        return VINF_F32
+    raise TypeError(f"libvinf tensors are float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (channels-last [F,H,W,C] storage)")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _fhwc(x: torch.Tensor):
+    if x.dim() != 4:
+        raise ValueError(f"expected a [F,H,W,C] tensor, got shape {tuple(x.shape)}")
+    return tuple(int(s) for s in x.shape)
+
+
+def groupnorm_workspace_bytes(F: int, H: int, W: int, C: int, groups: int, dtype: torch.dtype) -> int:
+    code = VINF_BF16 if dtype == torch.bfloat16 else VINF_F32
+    return int(load().vinf_groupnorm_workspace_bytes(F, H, W, C, groups, code))
+
+
+def groupnorm_global(x: torch.Tensor, groups: int, eps: float = 1e-5, gamma: torch.Tensor | None = None,
+                     beta: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     mean_out: torch.Tensor | None = None, rstd_out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None):
+    """GroupNorm with whole-video statistics.  Returns (y, mean[groups], rstd[groups])."""
+    _dev(x, "x")
+    F, H, W, C = _fhwc(x)
+    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    mean = torch.empty(groups, device=x.device, dtype=torch.float32) if mean_out is None else mean_out
+    rstd = torch.empty(groups, device=x.device, dtype=torch.float32) if rstd_out is None else rstd_out
+    need = groupnorm_workspace_bytes(F, H, W, C, groups, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().vinf_groupnorm_global(_ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(mean), _ptr(rstd), F, H, W, C,
+                                       groups, float(eps), _dtype_code(x), _ptr(workspace), ws_bytes,
+                                       _stream(x.device, stream))
+    _check("vinf_groupnorm_global", st)
+    return y, mean, rstd
+
+
+def temporal_conv3(x: torch.Tensor, weight: torch.Tensor, ctx_pre: torch.Tensor | None = None,
+                   ctx_post: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Kernel-3 temporal conv with context padding; weight is [3, C_out, C_in]."""
+    _dev(x, "x")
+    _dev(weight, "weight")
+    F, H, W, C = _fhwc(x)
+    if tuple(weight.shape) != (3, C, C) or weight.dtype != x.dtype:
+        raise ValueError(f"weight must be [3,{C},{C}] of {x.dtype}")
+    for name, c in (("ctx_pre", ctx_pre), ("ctx_post", ctx_post)):
+        if c is not None:
+            _dev(c, name)
+            if c.numel() != H * W * C or c.dtype != x.dtype:
+                raise ValueError(f"{name} must hold [H,W,C] = {H * W * C} values of {x.dtype}")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != C):
+        raise ValueError("bias must be float32 [C]")
+    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    st = load().vinf_temporal_conv3(_ptr(x), _ptr(ctx_pre), _ptr(ctx_post), _ptr(weight), _ptr(bias), _ptr(y), F, H,
+                                     W, C, _dtype_code(x), _stream(x.device, stream))
+    _check("vinf_temporal_conv3", st)
+    return y
+
+
+def dual_domain_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+                     head_dim: int = 64, n_local: int = 16, n_global: int = 16, scale: float = 0.0,
+                     stream=None) -> torch.Tensor:
+    """Dual-domain temporal attention over [F,H,W,C] q/k/v (already projected)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name)
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k and v must share shape and dtype")
+    F, H, W, C = _fhwc(q)
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    st = load().vinf_dual_domain_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), F, H, W, C, head_dim, n_local, n_global,
+                                       float(scale), _dtype_code(q), _stream(q.device, stream))
+    _check("vinf_dual_domain_attn", st)
+    return o
