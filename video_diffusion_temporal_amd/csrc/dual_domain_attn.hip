@@ -8,16 +8,17 @@
 // clamp(t-8, 0, F-16); the global frames are floor(i*F/16); the two lists are
 // concatenated, so a frame in both carries two softmax terms.
 //
-// bf16 kernel (dda_bf16).  One workgroup = 4 wave64s = one (location, head)
-// strip x 256 consecutive query frames, one query per lane.
+// bf16 kernel (dda_bf16).  Work item = one (location, head) strip x 256
+// consecutive query frames, one query per lane.
 //   * Staging: the strip's K rows for every local key of the 256 queries
 //     (<= 271 frames, 128 B each) and the 16 global K rows go to LDS; the V
 //     rows go to LDS re-packed as frame pairs, each dword holding
 //     (v[f][d], v[f+1][d]), so that the weighted sum over keys runs on
 //     v_dot2c_f32_bf16 with the softmax weights packed as bf16 pairs.  LDS
-//     rows are XOR-swizzled per 16-byte chunk so that lanes reading
-//     neighbouring frames hit distinct banks.  Every HBM load is a full
-//     128-byte row (one cache line) of one frame.
+//     rows are padded by 16 bytes (K rows 144 B, V pair rows 272 B) so that
+//     16 lanes reading neighbouring frames hit distinct banks, and every LDS
+//     read is a per-lane base plus an immediate offset (no address VALU).
+//     Every HBM load is a full 128-byte row (one cache line) of one frame.
 //   * Scores: q stays in 32 VGPRs as bf16 pairs; 32 keys x 32 v_dot2c each.
 //     The lane holds all 32 scores, so the softmax is lane-local: one max,
 //     exp2 with log2(e)*scale folded in, no cross-lane traffic.
@@ -27,9 +28,17 @@
 //     is the sum of the same bf16-rounded weights, so the output is an exact
 //     convex combination of the V rows up to fp32 rounding.
 //   * Output: fp32 -> bf16 (nearest even), 128-byte row per lane.
+//   * Pipelining: one persistent 512-thread workgroup per CU owns two LDS
+//     buffers (2 x 80 KB).  Its two 256-thread halves alternate: while one
+//     half stages its next work item (HBM -> LDS, plus its q rows into
+//     registers), the other computes from its own buffer; a workgroup barrier
+//     ends each phase.  HBM traffic and the VALU-bound compute overlap
+//     instead of alternating.
 // fp32 kernel (dda_f32): one query per thread, fp32 FMA, keys read through
 // the cache; used for float32 I/O.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -39,13 +48,16 @@ constexpr int DDA_D = 64;          // head dim
 constexpr int DDA_L = 16;          // local keys
 constexpr int DDA_G = 16;          // global keys
 constexpr int DDA_TQ = 256;        // queries per workgroup
-constexpr int DDA_KROWS = DDA_TQ + DDA_L;            // 272 local K rows
-constexpr int DDA_VPAIRS = (DDA_TQ + 19) / 2 + 1;    // 138 local V pair rows
-constexpr int DDA_LDS_KL = 0;
-constexpr int DDA_LDS_VP = DDA_LDS_KL + DDA_KROWS * 128;
-constexpr int DDA_LDS_KG = DDA_LDS_VP + DDA_VPAIRS * 256;
-constexpr int DDA_LDS_VG = DDA_LDS_KG + DDA_G * 128;
-constexpr int DDA_LDS_BYTES = DDA_LDS_VG + (DDA_G / 2) * 256;
+constexpr int DDA_KROWS = DDA_TQ + DDA_L - 1;        // 271 local K rows
+constexpr int DDA_VPAIRS = (DDA_TQ + 18) / 2;        // 137 local V pair rows
+constexpr int DDA_KSTR = 144;                        // padded K row (bytes)
+constexpr int DDA_VSTR = 272;                        // padded V pair row (bytes)
+constexpr int DDA_LDS_KG = 0;                        // 16 global K rows, 128 B
+constexpr int DDA_LDS_VG = DDA_LDS_KG + DDA_G * 128; // 8 global V pair rows, 256 B
+constexpr int DDA_LDS_KL = DDA_LDS_VG + (DDA_G / 2) * 256;
+constexpr int DDA_LDS_VP = DDA_LDS_KL + DDA_KROWS * DDA_KSTR;
+constexpr int DDA_LDS_BYTES = DDA_LDS_VP + DDA_VPAIRS * DDA_VSTR;
+static_assert(2 * DDA_LDS_BYTES <= 160 * 1024, "two workgroups per CU");
 
 __device__ __forceinline__ int dda_start(int t, int F) {
     int hi = F - DDA_L > 0 ? F - DDA_L : 0;
@@ -53,126 +65,143 @@ __device__ __forceinline__ int dda_start(int t, int F) {
     return st < 0 ? 0 : (st > hi ? hi : st);
 }
 
-// Byte offset of 16-byte chunk c of K row r (8 chunks per row).
-__device__ __forceinline__ int kl_off(int r, int c) { return DDA_LDS_KL + r * 128 + ((c ^ (r & 7)) << 4); }
-// Byte offset of 16-byte chunk c of V pair row p (16 chunks per row).
-__device__ __forceinline__ int vp_off(int p, int c) { return DDA_LDS_VP + p * 256 + ((c ^ (p & 7)) << 4); }
+__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-__device__ __forceinline__ u32x4_t gload(const uint16_t* base, int64_t elem) {
-    return *reinterpret_cast<const u32x4_t*>(base + elem);
+struct DdaItem {
+    int strip, t0;
+};
+
+__device__ __forceinline__ DdaItem dda_item(int idx, int nstrips) {
+    return DdaItem{idx % nstrips, (idx / nstrips) * DDA_TQ};
 }
 
-// Interleave two rows' dwords: (a.lo, b.lo) and (a.hi, b.hi).
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-__global__ void __launch_bounds__(256) dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int F,
-                                                   int S, int C, int nstrips, float sl2e) {
-    __shared__ __attribute__((aligned(16))) char lds[DDA_LDS_BYTES];
-    const uint32_t lb = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int strip = (int)(lb % (uint32_t)nstrips);
-    const int fblk = (int)(lb / (uint32_t)nstrips);
-    const int heads = C / DDA_D;
-    const int s = strip / heads, h = strip % heads;
-    const int64_t rs = (int64_t)S * C;                     // elements between frames
-    const int64_t col = (int64_t)s * C + h * DDA_D;        // strip's offset inside a frame
-    const int t0 = fblk * DDA_TQ;
-    const int tlast = min(t0 + DDA_TQ, F) - 1;
-    const int lo = dda_start(t0, F);
-    const int khi = dda_start(tlast, F) + DDA_L;           // stage K frames [lo, khi)
+// Stage one work item into `buf` (256 threads, lt = 0..255) and load the q row
+// of query t0 + lt into qv.
+__device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t* __restrict__ q,
+                                          const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int F,
+                                          int C, int64_t rs, int heads, DdaItem it, int lt, uint32_t (&qv)[32]) {
+    const int s = it.strip / heads, h = it.strip % heads;
+    const int64_t col = (int64_t)s * C + h * DDA_D;
+    const int tlast = min(it.t0 + DDA_TQ, F) - 1;
+    const int lo = dda_start(it.t0, F);
+    const int stl = dda_start(tlast, F);
+    const int nkr = stl + DDA_L - lo;             // K rows [lo, lo+nkr), <= 271
     const int plo = lo & ~1;
-    const int np = (dda_start(tlast, F) + DDA_L + 2 - plo + 1) >> 1;  // V pairs cover [plo, plo+2np)
-    const int tid = threadIdx.x;
-
-    // ---- stage local K rows ----
-    const int nk = (khi - lo) * 8;
+    const int np = (stl + DDA_L + 2 - plo) >> 1;  // V pairs cover [plo, plo+2np), <= 137
+    const int t = it.t0 + lt;
+    if (t < F) {
+        const uint16_t* qrow = q + t * rs + col;
 #pragma unroll
-    for (int it = 0; it < (DDA_KROWS * 8 + 255) / 256; ++it) {
-        int i = tid + it * 256;
-        if (i < nk) {
-            int r = i >> 3, c = i & 7, f = lo + r;
-            u32x4_t u = {0u, 0u, 0u, 0u};
-            if (f < F) u = gload(k, f * rs + col + c * 8);
-            *reinterpret_cast<u32x4_t*>(lds + kl_off(r, c)) = u;
+        for (int c = 0; c < 8; ++c) {
+            u32x4_t u = *reinterpret_cast<const u32x4_t*>(qrow + c * 8);
+            qv[4 * c] = u[0];
+            qv[4 * c + 1] = u[1];
+            qv[4 * c + 2] = u[2];
+            qv[4 * c + 3] = u[3];
         }
     }
-    // ---- stage local V as frame pairs ----
-    const int nv = np * 8;
+    // local K rows: this thread's chunk c = lt&7 of rows lt>>3 + 32*i
+    {
+        const int c = lt & 7, r0 = lt >> 3;
+        const uint16_t* src = k + col + (int64_t)(lo + r0) * rs + c * 8;
+        char* dst = buf + DDA_LDS_KL + r0 * DDA_KSTR + c * 16;
+        u32x4_t u[(DDA_KROWS + 31) / 32];
 #pragma unroll
-    for (int it = 0; it < (DDA_VPAIRS * 8 + 255) / 256; ++it) {
-        int i = tid + it * 256;
-        if (i < nv) {
-            int p = i >> 3, oc = i & 7, fa = plo + 2 * p, fb = fa + 1;
-            u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            if (fa < F) a = gload(v, fa * rs + col + oc * 8);
-            if (fb < F) b = gload(v, fb * rs + col + oc * 8);
-            u32x4_t w0 = {pair_lo(a[0], b[0]), pair_hi(a[0], b[0]), pair_lo(a[1], b[1]), pair_hi(a[1], b[1])};
-            u32x4_t w1 = {pair_lo(a[2], b[2]), pair_hi(a[2], b[2]), pair_lo(a[3], b[3]), pair_hi(a[3], b[3])};
-            *reinterpret_cast<u32x4_t*>(lds + vp_off(p, 2 * oc)) = w0;
-            *reinterpret_cast<u32x4_t*>(lds + vp_off(p, 2 * oc + 1)) = w1;
+        for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i) {
+            const int r = r0 + 32 * i;
+            u[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (r < nkr && lo + r < F) u[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(32 * i) * rs);
+        }
+#pragma unroll
+        for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i)
+            if (r0 + 32 * i < nkr) *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_KSTR) = u[i];
+    }
+    // local V as frame pairs: this thread's 8-dim group oc = lt&7 of pairs lt>>3 + 32*i
+    {
+        const int oc = lt & 7, p0 = lt >> 3;
+        const uint16_t* src = v + col + (int64_t)(plo + 2 * p0) * rs + oc * 8;
+        char* dst = buf + DDA_LDS_VP + p0 * DDA_VSTR + oc * 32;
+        u32x4_t a[(DDA_VPAIRS + 31) / 32], b[(DDA_VPAIRS + 31) / 32];
+#pragma unroll
+        for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
+            const int p = p0 + 32 * i, fa = plo + 2 * p;
+            a[i] = u32x4_t{0u, 0u, 0u, 0u};
+            b[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (p < np && fa < F) a[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i) * rs);
+            if (p < np && fa + 1 < F) b[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i + 1) * rs);
+        }
+#pragma unroll
+        for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
+            if (p0 + 32 * i < np) {
+                u32x4_t w0 = {perm_lo(a[i][0], b[i][0]), perm_hi(a[i][0], b[i][0]), perm_lo(a[i][1], b[i][1]),
+                              perm_hi(a[i][1], b[i][1])};
+                u32x4_t w1 = {perm_lo(a[i][2], b[i][2]), perm_hi(a[i][2], b[i][2]), perm_lo(a[i][3], b[i][3]),
+                              perm_hi(a[i][3], b[i][3])};
+                *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR) = w0;
+                *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR + 16) = w1;
+            }
         }
     }
-    // ---- stage global K rows and V pairs ----
-    if (tid < DDA_G * 8) {
-        int i = tid >> 3, c = tid & 7;
-        int f = (int)(((int64_t)i * F) / DDA_G);
-        *reinterpret_cast<u32x4_t*>(lds + DDA_LDS_KG + i * 128 + c * 16) = gload(k, f * rs + col + c * 8);
-    } else if (tid < DDA_G * 8 + (DDA_G / 2) * 8) {
-        int j = tid - DDA_G * 8;
-        int p = j >> 3, oc = j & 7;
-        int fa = (int)(((int64_t)(2 * p) * F) / DDA_G), fb = (int)(((int64_t)(2 * p + 1) * F) / DDA_G);
-        u32x4_t a = gload(v, fa * rs + col + oc * 8), b = gload(v, fb * rs + col + oc * 8);
-        u32x4_t w0 = {pair_lo(a[0], b[0]), pair_hi(a[0], b[0]), pair_lo(a[1], b[1]), pair_hi(a[1], b[1])};
-        u32x4_t w1 = {pair_lo(a[2], b[2]), pair_hi(a[2], b[2]), pair_lo(a[3], b[3]), pair_hi(a[3], b[3])};
-        *reinterpret_cast<u32x4_t*>(lds + DDA_LDS_VG + p * 256 + (2 * oc) * 16) = w0;
-        *reinterpret_cast<u32x4_t*>(lds + DDA_LDS_VG + p * 256 + (2 * oc + 1) * 16) = w1;
+    // global K rows (threads 0..127) and V pairs (threads 128..191)
+    if (lt < DDA_G * 8) {
+        const int i = lt >> 3, c = lt & 7;
+        const int f = (int)(((int64_t)i * F) / DDA_G);
+        *reinterpret_cast<u32x4_t*>(buf + DDA_LDS_KG + i * 128 + c * 16) =
+            *reinterpret_cast<const u32x4_t*>(k + col + f * rs + c * 8);
+    } else if (lt < DDA_G * 8 + (DDA_G / 2) * 8) {
+        const int j = lt - DDA_G * 8;
+        const int p = j >> 3, oc = j & 7;
+        const int fa = (int)(((int64_t)(2 * p) * F) / DDA_G), fb = (int)(((int64_t)(2 * p + 1) * F) / DDA_G);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(v + col + fa * rs + oc * 8);
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(v + col + fb * rs + oc * 8);
+        u32x4_t w0 = {perm_lo(a[0], b[0]), perm_hi(a[0], b[0]), perm_lo(a[1], b[1]), perm_hi(a[1], b[1])};
+        u32x4_t w1 = {perm_lo(a[2], b[2]), perm_hi(a[2], b[2]), perm_lo(a[3], b[3]), perm_hi(a[3], b[3])};
+        char* dst = buf + DDA_LDS_VG + p * 256 + oc * 32;
+        *reinterpret_cast<u32x4_t*>(dst) = w0;
+        *reinterpret_cast<u32x4_t*>(dst + 16) = w1;
     }
-    __syncthreads();
+}
 
-    const int t = t0 + tid;
+// Compute query t0 + lt of a staged work item from `buf`.
+__device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16_t* __restrict__ o, int F, int C,
+                                            int64_t rs, int heads, DdaItem it, int lt, const uint32_t (&qv)[32],
+                                            float sl2e) {
+    const int t = it.t0 + lt;
     if (t >= F) return;
+    const int s = it.strip / heads, h = it.strip % heads;
+    const int64_t col = (int64_t)s * C + h * DDA_D;
+    const int lo = dda_start(it.t0, F);
+    const int plo = lo & ~1;
     const int nl = F < DDA_L ? F : DDA_L;
     const int st = dda_start(t, F);
 
-    // q row as 32 bf16 pairs
-    uint32_t qv[32];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        u32x4_t u = gload(q, t * rs + col + c * 8);
-        qv[4 * c] = u[0];
-        qv[4 * c + 1] = u[1];
-        qv[4 * c + 2] = u[2];
-        qv[4 * c + 3] = u[3];
-    }
-
-    // ---- scores ----
+    // ---- scores: one K row (8 x 16 B) per key; the next row's reads are
+    // issued before the current row's dot products ----
     float sc[DDA_L + DDA_G];
+    const char* krow = buf + DDA_LDS_KL + (st - lo) * DDA_KSTR;
+    auto key_row = [&](int i) -> const char* {
+        return i < DDA_L ? krow + i * DDA_KSTR : buf + DDA_LDS_KG + (i - DDA_L) * 128;
+    };
+    u32x4_t kb[2][8];
 #pragma unroll
-    for (int j = 0; j < DDA_L + DDA_G; ++j) sc[j] = 0.f;
-    const int kr0 = st - lo;
+    for (int c = 0; c < 8; ++c) kb[0][c] = *reinterpret_cast<const u32x4_t*>(key_row(0) + c * 16);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int i = 0; i < DDA_L + DDA_G; ++i) {
+        if (i + 1 < DDA_L + DDA_G) {
 #pragma unroll
-        for (int i = 0; i < DDA_L; ++i) {
-            u32x4_t u = *reinterpret_cast<const u32x4_t*>(lds + kl_off(kr0 + i, c));
-            float a = sc[i];
+            for (int c = 0; c < 8; ++c) kb[(i + 1) & 1][c] = *reinterpret_cast<const u32x4_t*>(key_row(i + 1) + c * 16);
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const u32x4_t u = kb[i & 1][c];
             a = dot2_bf16(qv[4 * c], u[0], a);
             a = dot2_bf16(qv[4 * c + 1], u[1], a);
             a = dot2_bf16(qv[4 * c + 2], u[2], a);
             a = dot2_bf16(qv[4 * c + 3], u[3], a);
-            sc[i] = a;
         }
-#pragma unroll
-        for (int i = 0; i < DDA_G; ++i) {
-            u32x4_t u = *reinterpret_cast<const u32x4_t*>(lds + DDA_LDS_KG + i * 128 + c * 16);
-            float a = sc[DDA_L + i];
-            a = dot2_bf16(qv[4 * c], u[0], a);
-            a = dot2_bf16(qv[4 * c + 1], u[1], a);
-            a = dot2_bf16(qv[4 * c + 2], u[2], a);
-            a = dot2_bf16(qv[4 * c + 3], u[3], a);
-            sc[DDA_L + i] = a;
-        }
+        sc[i] = a;
     }
 
     // ---- lane-local softmax (base 2, scale folded in) ----
@@ -205,37 +234,82 @@ __global__ void __launch_bounds__(256) dda_bf16(const uint16_t* __restrict__ q, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) den = dot2_bf16(wg[i], ones, den);
 
-    // ---- weighted sum of V ----
+    // ---- weighted sum of V: 9 local + 8 global pair rows, next row's
+    // reads issued before the current row's dot products ----
     float acc[DDA_D];
 #pragma unroll
     for (int d = 0; d < DDA_D; ++d) acc[d] = 0.f;
-    const int pb = (st - plo) >> 1;
+    const char* vrow = buf + DDA_LDS_VP + ((st - plo) >> 1) * DDA_VSTR;
+    auto val_row = [&](int j) -> const char* {
+        return j < 9 ? vrow + j * DDA_VSTR : buf + DDA_LDS_VG + (j - 9) * 256;
+    };
+    // half rows (32 dims, 8 x 16 B) double-buffered: step 2j + hh reads
+    // dims 32*hh.. of pair row j
+    u32x4_t vb[2][8];
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
+    for (int c = 0; c < 8; ++c) vb[0][c] = *reinterpret_cast<const u32x4_t*>(val_row(0) + c * 16);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            u32x4_t u = *reinterpret_cast<const u32x4_t*>(lds + vp_off(pb + j, c));
+    for (int step = 0; step < 34; ++step) {
+        const int j = step >> 1, hh = step & 1;
+        if (step + 1 < 34) {
+            const int jn = (step + 1) >> 1, hn = (step + 1) & 1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[4 * c + e] = dot2_bf16(wl[j], u[e], acc[4 * c + e]);
+            for (int c = 0; c < 8; ++c)
+                vb[(step + 1) & 1][c] = *reinterpret_cast<const u32x4_t*>(val_row(jn) + hn * 128 + c * 16);
         }
-    }
+        const uint32_t wj = j < 9 ? wl[j] : wg[j - 9];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+        for (int c = 0; c < 8; ++c) {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            u32x4_t u = *reinterpret_cast<const u32x4_t*>(lds + DDA_LDS_VG + i * 256 + c * 16);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[4 * c + e] = dot2_bf16(wg[i], u[e], acc[4 * c + e]);
+            for (int e = 0; e < 4; ++e)
+                acc[32 * hh + 4 * c + e] = dot2_bf16(wj, vb[step & 1][c][e], acc[32 * hh + 4 * c + e]);
         }
     }
 
     const float inv = 1.f / den;
+    uint16_t* orow = o + t * rs + col;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         u32x4_t w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[8 * c + 2 * e] * inv, acc[8 * c + 2 * e + 1] * inv);
-        *reinterpret_cast<u32x4_t*>(o + t * rs + col + c * 8) = w;
+        *reinterpret_cast<u32x4_t*>(orow + c * 8) = w;
+    }
+}
+
+// Persistent, two-phase pipelined kernel: workgroup w takes items
+// w, w + G, w + 2G, ... (G = gridDim.x); its half g (threads 256g..256g+255)
+// takes the items with odd (g = 1) or even (g = 0) position in that list.
+// Phase p: half 0 stages its item p/2 (p even) or computes item (p-1)/2 (p
+// odd); half 1 stages item (p-1)/2 (p odd) or computes item (p-2)/2 (p even,
+// p >= 2).  Every thread runs every phase and barrier.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+         uint16_t* __restrict__ o, int F, int S, int C, int nstrips, int nitems, float sl2e) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * DDA_LDS_BYTES];
+    const int heads = C / DDA_D;
+    const int64_t rs = (int64_t)S * C;
+    const int half = threadIdx.x >> 8, lt = threadIdx.x & 255;
+    char* buf = lds + half * DDA_LDS_BYTES;
+    const int G = gridDim.x, w = blockIdx.x;
+    const int mine = w < nitems ? (nitems - w + G - 1) / G : 0;     // items of this workgroup
+    const int jh = (mine - half + 1) / 2;                            // items of this half
+    const int j0 = (mine + 1) / 2, j1 = mine / 2;
+    const int phases = max(2 * j0, 2 * j1 + 1);
+    uint32_t qv[32];
+    for (int p = 0; p < phases; ++p) {
+        const int rel = p - half;                 // half 0: rel = p, half 1: rel = p - 1
+        if (rel >= 0) {
+            const int j = rel >> 1;
+            if (j < jh) {
+                const DdaItem it = dda_item(w + (2 * j + half) * G, nstrips);
+                if ((rel & 1) == 0)
+                    dda_stage(buf, q, k, v, F, C, rs, heads, it, lt, qv);
+                else
+                    dda_compute(buf, o, F, C, rs, heads, it, lt, qv, sl2e);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -293,11 +367,16 @@ vinf_status launch_dda(const void* q, const void* k, const void* v, void* o, int
     if (dt == VINF_BF16) {
         const int nstrips = S * heads;
         const int nfb = (F + DDA_TQ - 1) / DDA_TQ;
-        const int64_t blocks = (int64_t)nstrips * nfb;
-        if (blocks > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "dual_domain_attn: grid too large");
-        hipLaunchKernelGGL(dda_bf16, dim3((uint32_t)blocks), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), F, S, C, nstrips, sl2e);
+        const int64_t items = (int64_t)nstrips * nfb;
+        if (items > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "dual_domain_attn: too many work items");
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            return fail(VINF_ERR_HIP, "dual_domain_attn: cannot query the device");
+        // one persistent workgroup per CU, each with at least two items
+        const int64_t grid = std::min<int64_t>(cus, (items + 1) / 2);
+        hipLaunchKernelGGL(dda_bf16, dim3((uint32_t)grid), dim3(512), 0, st, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
+                           F, S, C, nstrips, (int)items, sl2e);
     } else {
         const int64_t nq = (int64_t)F * S * heads;
         const int64_t blocks = (nq + 63) / 64;
