@@ -10,100 +10,123 @@
 //
 // bf16 kernel (conv3_bf16): an implicit GEMM with M = F*S output voxels,
 // N = C_out, K = 3*C_in, on v_mfma_f32_16x16x32_bf16.
-//   * A workgroup tile is 8 frames x 16 locations (128 rows of M) by BN
-//     output channels.  For each 32-channel slice of C_in it stages 10 frames
-//     x 16 locations of x (the 8 frames plus one halo frame per side) and the
-//     three taps' weight rows into LDS; a tap is then a shift of the A operand
-//     by one frame (16 LDS rows), so the three taps share one staged tile.
-//   * 4 waves as 2 (M) x 2 (N).  Each wave's 64 rows are 4 frames; with the
-//     tap shift it reads 6 A fragments and 3*BN/32 B fragments per slice for
-//     3*4*BN/32 MFMAs.  The next slice's global loads are issued before the
-//     current slice's MFMAs (register prefetch).
-//   * LDS rows are 64 bytes with an XOR swizzle of the 16-byte chunks.
-//   * Workgroup ids are remapped so that the N tiles of one M tile and the
-//     next frame block of the same locations run on the same XCD (shared L2
-//     for the re-read x rows and halos).
+//   * A tile is 16 frames x 16 locations (256 rows of M) by BN = 32*NF output
+//     channels (all of C_out when NF = 10 and C = 320).  For each 32-channel
+//     slice of C_in, 18 frames x 16 locations of x (the 16 frames plus one
+//     halo frame per side) and the three taps' weight rows are staged in LDS;
+//     a tap is then a shift of the x operand by one frame (16 LDS rows), so
+//     the three taps share one staged tile.
+//   * Staging uses buffer_load_dwordx4 ... lds (HBM/L2 -> LDS without
+//     VGPRs).  One wave instruction fills one frame's 16 locations; frames
+//     outside the video come from ctx_pre / ctx_post or read as zeros
+//     (num_records = 0), locations past S read as zeros (out of range).
+//   * LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot
+//     c ^ ((r >> 2) & 3), which keeps 16-lane fragment reads conflict-free and
+//     makes each lane's slot a constant, so all fragment reads use immediate
+//     offsets.
+//   * 8 waves as 4 (M) x 2 (N); a wave owns 4 frames x 16*NF channels and
+//     reads 6 x fragments (4 frames + the two tap shifts) and 3*NF weight
+//     fragments per slice.  The weight fragment is the MFMA's A operand, so
+//     each lane's accumulator holds 4 consecutive output channels of one
+//     voxel and the epilogue writes 8-byte pieces of channel-contiguous rows.
+//   * Persistent: one 512-thread workgroup per CU walks a contiguous range of
+//     tiles (consecutive frame blocks of the same locations, so halo frames
+//     are L2 hits); LDS is double-buffered across slices and tiles with one
+//     barrier per slice, and the next slice's loads are in flight while the
+//     current one is multiplied.
 // fp32 kernel (conv3_f32): one output element per thread, fp32 FMA.
+#include <algorithm>
+
 #include "common.h"
 
 namespace vinf {
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
-constexpr int CV_TF = 8;                  // frames per tile
-constexpr int CV_TP = 16;                 // locations per tile
-constexpr int CV_AROWS = (CV_TF + 2) * CV_TP;  // 160 staged x rows
-constexpr int CV_BK = 32;                 // C_in slice
-
-__device__ __forceinline__ int cv_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
+constexpr int CV_TF = 16;                       // frames per tile
+constexpr int CV_TP = 16;                       // locations per tile
+constexpr int CV_AROWS = (CV_TF + 2) * CV_TP;   // 288 staged x rows
+constexpr int CV_BK = 32;                       // C_in slice
 
 template <int NF>
-__global__ void __launch_bounds__(256) conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre,
-                                                  const uint16_t* __restrict__ post,
-                                                  const uint16_t* __restrict__ w, const float* __restrict__ bias,
-                                                  uint16_t* __restrict__ y, int F, int S, int C, int nfb, int ntn) {
-    constexpr int BN = 32 * NF;                   // output channels per workgroup
-    constexpr int B_ITEMS = 3 * BN * 4;           // 16-byte chunks of the weight tile
-    constexpr int B_IT = (B_ITEMS + 255) / 256;
-    constexpr int A_ITEMS = CV_AROWS * 4;         // 640
-    constexpr int A_IT = (A_ITEMS + 255) / 256;   // 3
-    __shared__ __attribute__((aligned(16))) char sa[CV_AROWS * 64];
-    __shared__ __attribute__((aligned(16))) char sb[3 * BN * 64];
+struct ConvLds {
+    static constexpr int BN = 32 * NF;
+    static constexpr int A_BYTES = CV_AROWS * 64;
+    static constexpr int B_BYTES = 3 * BN * 64;
+    static constexpr int BUF = A_BYTES + B_BYTES;
+};
 
-    const uint32_t lb = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int nt = (int)(lb % (uint32_t)ntn);
-    const int mt = (int)(lb / (uint32_t)ntn);
-    const int fb = mt % nfb, lbk = mt / nfb;
-    const int f0 = fb * CV_TF, s0 = lbk * CV_TP, n0 = nt * BN;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t cv_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int NF>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, const uint16_t* __restrict__ post,
+           const uint16_t* __restrict__ w, const float* __restrict__ bias, uint16_t* __restrict__ y, int F, int S,
+           int C, int nfb, int nlb, int ntn) {
+    using L = ConvLds<NF>;
+    constexpr int BN = L::BN;
+    constexpr int B_INSTR = 3 * BN / 16;        // wave instructions per weight slice (16 rows each)
+    __shared__ __attribute__((aligned(1024))) char lds[2 * L::BUF];
+
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv & 1, wn = wv >> 1;
-    const int64_t rs = (int64_t)S * C;
+    const int wm = wv & 3, wn = wv >> 2;
+    const int lr = lane & 15, lc = lane >> 4;
+    const int nk = C / CV_BK;
+    const int ntiles = nfb * nlb * ntn;
+    // contiguous range of tiles per workgroup
+    const int t_begin = (int)(((int64_t)ntiles * blockIdx.x) / gridDim.x);
+    const int t_end = (int)(((int64_t)ntiles * (blockIdx.x + 1)) / gridDim.x);
+    const uint32_t frame_bytes = (uint32_t)S * (uint32_t)C * 2u;
+    const __amdgpu_buffer_rsrc_t wr = cv_rsrc(w, 3u * (uint32_t)C * (uint32_t)C * 2u);
 
-    // Global source of staged A item i: pointer or null (zeros).
-    auto a_src = [&](int i) -> const uint16_t* {
-        int r = i >> 2, c = i & 3;
-        int f = f0 - 1 + r / CV_TP, s = s0 + r % CV_TP;
-        if (s >= S) return nullptr;
-        if (f < 0) return pre ? pre + (int64_t)s * C + c * 8 : nullptr;
-        if (f >= F) return (f == F && post) ? post + (int64_t)s * C + c * 8 : nullptr;
-        return x + f * rs + (int64_t)s * C + c * 8;
-    };
-    const uint16_t* asrc[A_IT];
-#pragma unroll
-    for (int it = 0; it < A_IT; ++it) {
-        int i = tid + it * 256;
-        asrc[it] = i < A_ITEMS ? a_src(i) : nullptr;
-    }
-    const uint16_t* bsrc[B_IT];
-#pragma unroll
-    for (int it = 0; it < B_IT; ++it) {
-        int i = tid + it * 256;
-        int r = i >> 2, c = i & 3;          // r = tap*BN + co
-        int tap = r / BN, co = r % BN;
-        bsrc[it] = i < B_ITEMS ? w + ((int64_t)tap * C + n0 + co) * C + c * 8 : nullptr;
-    }
+    // Staging lane mapping: lane l of a wave instruction fills LDS slot l of a
+    // 1 KB block = row (16*i + l/4), slot l%4, i.e. chunk (l&3) ^ (l>>4).
+    const int st_row = lane >> 2;
+    const int st_chunk = (lane & 3) ^ (lane >> 4);
+    // Fragment reads: row = base + lr, slot = lc ^ (lr >> 2).
+    const int rd_off = lr * 64 + ((lc ^ (lr >> 2)) << 4);
 
-    u32x4_t ra[A_IT], rb[B_IT];
-    auto gload = [&](int kc) {
-#pragma unroll
-        for (int it = 0; it < A_IT; ++it) {
-            ra[it] = u32x4_t{0u, 0u, 0u, 0u};
-            if (asrc[it]) ra[it] = *reinterpret_cast<const u32x4_t*>(asrc[it] + kc * CV_BK);
-        }
-#pragma unroll
-        for (int it = 0; it < B_IT; ++it)
-            if (bsrc[it]) rb[it] = *reinterpret_cast<const u32x4_t*>(bsrc[it] + kc * CV_BK);
+    auto tile_coords = [&](int t, int& f0, int& s0, int& n0) {
+        const int nt = t % ntn, m = t / ntn;
+        f0 = (m % nfb) * CV_TF;
+        s0 = (m / nfb) * CV_TP;
+        n0 = nt * BN;
     };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int it = 0; it < A_IT; ++it) {
-            int i = tid + it * 256;
-            if (i < A_ITEMS) *reinterpret_cast<u32x4_t*>(sa + cv_off(i >> 2, i & 3)) = ra[it];
+
+    // Issue the loads of slice kc of tile t into buffer b.
+    auto issue = [&](int t, int kc, int b) {
+        int f0, s0, n0;
+        tile_coords(t, f0, s0, n0);
+        char* abuf = lds + b * L::BUF;
+        char* bbuf = abuf + L::A_BYTES;
+        const uint32_t loc_off = ((uint32_t)(s0 + st_row) * (uint32_t)C + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
+        const uint32_t voff = s0 + st_row < S ? loc_off : frame_bytes;   // past the end: zeros
+        for (int i = wv; i < CV_TF + 2; i += 8) {                       // one frame per instruction
+            const int f = f0 - 1 + i;
+            const void* base = x;
+            uint32_t nrec = 0;
+            if (f >= 0 && f < F) {
+                base = x + (int64_t)f * S * C;
+                nrec = frame_bytes;
+            } else if (f == -1 && pre) {
+                base = pre;
+                nrec = frame_bytes;
+            } else if (f == F && post) {
+                base = post;
+                nrec = frame_bytes;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(cv_rsrc(base, nrec),
+                                                     (__attribute__((address_space(3))) void*)(abuf + i * 1024), 16,
+                                                     voff, 0, 0, 0);
         }
-#pragma unroll
-        for (int it = 0; it < B_IT; ++it) {
-            int i = tid + it * 256;
-            if (i < B_ITEMS) *reinterpret_cast<u32x4_t*>(sb + cv_off(i >> 2, i & 3)) = rb[it];
+        for (int i = wv; i < B_INSTR; i += 8) {                         // 16 weight rows per instruction
+            const int r = 16 * i + st_row;                              // r = tap*BN + co
+            const int tap = r / BN, co = r - tap * BN;
+            const uint32_t off = ((uint32_t)((tap * C + n0 + co) * C) + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(bbuf + i * 1024),
+                                                     16, off, 0, 0, 0);
         }
     };
 
@@ -113,50 +136,60 @@ __global__ void __launch_bounds__(256) conv3_bf16(const uint16_t* __restrict__ x
 #pragma unroll
         for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = C / CV_BK;
-    const int lr = lane & 15, lc = lane >> 4;
-    gload(0);
-    for (int kc = 0; kc < nk; ++kc) {
-        __syncthreads();  // previous slice's fragments are consumed
-        lstore();
-        __syncthreads();
-        if (kc + 1 < nk) gload(kc + 1);
-        bf16x8v a[6];
+    if (t_begin < t_end) issue(t_begin, 0, 0);
+    int g = 0;  // slice counter across tiles (selects the buffer)
+    for (int t = t_begin; t < t_end; ++t) {
+        for (int kc = 0; kc < nk; ++kc, ++g) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of slice g are in LDS
+            __syncthreads();                      // everyone's are; slice g-1 is no longer read
+            if (kc + 1 < nk)
+                issue(t, kc + 1, (g + 1) & 1);
+            else if (t + 1 < t_end)
+                issue(t + 1, 0, (g + 1) & 1);
+            const char* abuf = lds + (g & 1) * L::BUF;
+            const char* bbuf = abuf + L::A_BYTES;
+            bf16x8v a[6];
 #pragma unroll
-        for (int j = 0; j < 6; ++j)
-            a[j] = *reinterpret_cast<const bf16x8v*>(sa + cv_off(wm * 64 + j * 16 + lr, lc));
+            for (int j = 0; j < 6; ++j)
+                a[j] = *reinterpret_cast<const bf16x8v*>(abuf + (wm * 64 + j * 16) * 64 + rd_off);
 #pragma unroll
-        for (int tap = 0; tap < 3; ++tap) {
-            bf16x8v b[NF];
-#pragma unroll
-            for (int ni = 0; ni < NF; ++ni)
-                b[ni] = *reinterpret_cast<const bf16x8v*>(sb + cv_off(tap * BN + wn * 16 * NF + ni * 16 + lr, lc));
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int tap = 0; tap < 3; ++tap) {
+                bf16x8v b[NF];
 #pragma unroll
                 for (int ni = 0; ni < NF; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi + tap], b[ni], acc[mi][ni], 0, 0, 0);
+                    b[ni] = *reinterpret_cast<const bf16x8v*>(bbuf + (tap * BN + wn * 16 * NF + ni * 16) * 64 + rd_off);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < NF; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ni], a[mi + tap], acc[mi][ni], 0, 0, 0);
+            }
         }
-    }
-
-    // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, locations
-    // s0 + 4*(lane/16) + i, channel n0 + wn*16*NF + ni*16 + lane%16.
+        // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, location
+        // s0 + lane%16, channels n0 + wn*16*NF + ni*16 + 4*(lane/16) + 0..3.
+        int f0, s0, n0;
+        tile_coords(t, f0, s0, n0);
+        const int s = s0 + lr;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        int f = f0 + 4 * wm + mi;
-        if (f >= F) continue;
+        for (int mi = 0; mi < 4; ++mi) {
+            const int f = f0 + 4 * wm + mi;
 #pragma unroll
-        for (int ni = 0; ni < NF; ++ni) {
-            int n = n0 + wn * 16 * NF + ni * 16 + lr;
-            float bv = bias ? bias[n] : 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int s = s0 + 4 * lc + i;
-                if (s < S) {
-                    bf16x2_t r;
-                    r[0] = (__bf16)(acc[mi][ni][i] + bv);
-                    y[f * rs + (int64_t)s * C + n] = __builtin_bit_cast(uint16_t, r[0]);
+            for (int ni = 0; ni < NF; ++ni) {
+                const int n = n0 + wn * 16 * NF + ni * 16 + 4 * lc;
+                if (f < F && s < S) {
+                    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+                    if (bias) {
+                        b0 = bias[n];
+                        b1 = bias[n + 1];
+                        b2 = bias[n + 2];
+                        b3 = bias[n + 3];
+                    }
+                    uint2 o;
+                    o.x = pack_bf16x2(acc[mi][ni][0] + b0, acc[mi][ni][1] + b1);
+                    o.y = pack_bf16x2(acc[mi][ni][2] + b2, acc[mi][ni][3] + b3);
+                    *reinterpret_cast<uint2*>(y + ((int64_t)f * S + s) * C + n) = o;
                 }
+                acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
     }
@@ -196,30 +229,38 @@ namespace vinf_host {
 using namespace vinf;
 
 template <int NF>
-static void launch_bf16(const void* x, const void* pre, const void* post, const void* w, const float* bias, void* y,
-                        int F, int S, int C, hipStream_t st, int64_t* blocks_out) {
+static vinf_status launch_bf16(const void* x, const void* pre, const void* post, const void* w, const float* bias,
+                               void* y, int F, int S, int C, hipStream_t st) {
     const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP, ntn = C / (32 * NF);
-    const int64_t blocks = (int64_t)nfb * nlb * ntn;
-    *blocks_out = blocks;
-    if (blocks > 0x7fffffff) return;
-    hipLaunchKernelGGL(conv3_bf16<NF>, dim3((uint32_t)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(x),
+    const int64_t tiles = (int64_t)nfb * nlb * ntn;
+    if (tiles > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: too many tiles");
+    if ((uint64_t)S * C * 2 >= 0x80000000ull || (uint64_t)3 * C * C * 2 >= 0x80000000ull)
+        return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: one frame or the weights exceed 2 GiB");
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(VINF_ERR_HIP, "temporal_conv3: cannot query the device");
+    const int grid = (int)std::min<int64_t>(cus, tiles);
+    hipLaunchKernelGGL(conv3_bf16<NF>, dim3(grid), dim3(512), 0, st, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(pre), static_cast<const uint16_t*>(post),
-                       static_cast<const uint16_t*>(w), bias, static_cast<uint16_t*>(y), F, S, C, nfb, ntn);
+                       static_cast<const uint16_t*>(w), bias, static_cast<uint16_t*>(y), F, S, C, nfb, nlb, ntn);
+    return VINF_OK;
 }
 
 vinf_status launch_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
                          const float* bias, void* y, int F, int S, int C, vinf_dtype dt, hipStream_t st) {
     if (dt == VINF_BF16) {
-        int64_t blocks = 0;
-        if (C % 160 == 0)
-            launch_bf16<5>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st, &blocks);
+        vinf_status r;
+        if (C % 320 == 0)
+            r = launch_bf16<10>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+        else if (C % 256 == 0)
+            r = launch_bf16<8>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         else if (C % 128 == 0)
-            launch_bf16<4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st, &blocks);
+            r = launch_bf16<4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         else if (C % 64 == 0)
-            launch_bf16<2>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st, &blocks);
+            r = launch_bf16<2>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         else
-            launch_bf16<1>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st, &blocks);
-        if (blocks > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: grid too large");
+            r = launch_bf16<1>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+        if (r != VINF_OK) return r;
     } else {
         const int64_t n = (int64_t)F * S * C;
         const int64_t blocks = (n + 255) / 256;
