@@ -289,7 +289,7 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     __shared__ __attribute__((aligned(16))) char lds[2 * DDA_LDS_BYTES];
     const int heads = C / DDA_D;
     const int64_t rs = (int64_t)S * C;
-    const int half = threadIdx.x >> 8, lt = threadIdx.x & 255;
+    const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), lt = threadIdx.x & 255;
     char* buf = lds + half * DDA_LDS_BYTES;
     const int G = gridDim.x, w = blockIdx.x;
     const int mine = w < nitems ? (nitems - w + G - 1) / G : 0;     // items of this workgroup

@@ -21,9 +21,10 @@
 //     outside the video come from ctx_pre / ctx_post or read as zeros
 //     (num_records = 0), locations past S read as zeros (out of range).
 //   * LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot
-//     c ^ ((r >> 2) & 3), which keeps 16-lane fragment reads conflict-free and
-//     makes each lane's slot a constant, so all fragment reads use immediate
-//     offsets.
+//     c ^ ((r >> 1) & 3), which keeps fragment reads (16 consecutive rows,
+//     one chunk per lane group) free of bank conflicts (measured with the
+//     LDS bank-conflict counter) and makes each lane's slot a constant, so
+//     all fragment reads use immediate offsets.
 //   * 8 waves as 4 (M) x 2 (N); a wave owns 4 frames x 16*NF channels and
 //     reads 6 x fragments (4 frames + the two tap shifts) and 3*NF weight
 //     fragments per slice.  The weight fragment is the MFMA's A operand, so
@@ -48,9 +49,9 @@ constexpr int CV_TP = 16;                       // locations per tile
 constexpr int CV_AROWS = (CV_TF + 2) * CV_TP;   // 288 staged x rows
 constexpr int CV_BK = 32;                       // C_in slice
 
-template <int NF>
+template <int NF, int WN>
 struct ConvLds {
-    static constexpr int BN = 32 * NF;
+    static constexpr int BN = 16 * NF * WN;
     static constexpr int A_BYTES = CV_AROWS * 64;
     static constexpr int B_BYTES = 3 * BN * 64;
     static constexpr int BUF = A_BYTES + B_BYTES;
@@ -60,18 +61,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t cv_rsrc(const void* base, uint
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int NF>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int NF, int WN>
+__global__ void __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(WN, WN)))
 conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, const uint16_t* __restrict__ post,
            const uint16_t* __restrict__ w, const float* __restrict__ bias, uint16_t* __restrict__ y, int F, int S,
            int C, int nfb, int nlb, int ntn) {
-    using L = ConvLds<NF>;
+    using L = ConvLds<NF, WN>;
     constexpr int BN = L::BN;
+    constexpr int NW = 4 * WN;                  // waves: 4 along M x WN along N
     constexpr int B_INSTR = 3 * BN / 16;        // wave instructions per weight slice (16 rows each)
     __shared__ __attribute__((aligned(1024))) char lds[2 * L::BUF];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv & 3, wn = wv >> 2;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    const int wm = wv & 3, wn = wv >> 2;          // wave (M, N) position
     const int lr = lane & 15, lc = lane >> 4;
     const int nk = C / CV_BK;
     const int ntiles = nfb * nlb * ntn;
@@ -82,11 +85,11 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
     const __amdgpu_buffer_rsrc_t wr = cv_rsrc(w, 3u * (uint32_t)C * (uint32_t)C * 2u);
 
     // Staging lane mapping: lane l of a wave instruction fills LDS slot l of a
-    // 1 KB block = row (16*i + l/4), slot l%4, i.e. chunk (l&3) ^ (l>>4).
+    // 1 KB block = row (16*i + l/4), slot l%4, i.e. chunk (l&3) ^ ((l>>3)&3).
     const int st_row = lane >> 2;
-    const int st_chunk = (lane & 3) ^ (lane >> 4);
-    // Fragment reads: row = base + lr, slot = lc ^ (lr >> 2).
-    const int rd_off = lr * 64 + ((lc ^ (lr >> 2)) << 4);
+    const int st_chunk = (lane & 3) ^ ((lane >> 3) & 3);
+    // Fragment reads: row = base + lr (base a multiple of 16), slot = lc ^ ((lr >> 1) & 3).
+    const int rd_off = lr * 64 + ((lc ^ ((lr >> 1) & 3)) << 4);
 
     auto tile_coords = [&](int t, int& f0, int& s0, int& n0) {
         const int nt = t % ntn, m = t / ntn;
@@ -103,7 +106,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         char* bbuf = abuf + L::A_BYTES;
         const uint32_t loc_off = ((uint32_t)(s0 + st_row) * (uint32_t)C + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
         const uint32_t voff = s0 + st_row < S ? loc_off : frame_bytes;   // past the end: zeros
-        for (int i = wv; i < CV_TF + 2; i += 8) {                       // one frame per instruction
+        for (int i = wv; i < CV_TF + 2; i += NW) {                      // one frame per instruction
             const int f = f0 - 1 + i;
             const void* base = x;
             uint32_t nrec = 0;
@@ -121,7 +124,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
                                                      (__attribute__((address_space(3))) void*)(abuf + i * 1024), 16,
                                                      voff, 0, 0, 0);
         }
-        for (int i = wv; i < B_INSTR; i += 8) {                         // 16 weight rows per instruction
+        for (int i = wv; i < B_INSTR; i += NW) {                        // 16 weight rows per instruction
             const int r = 16 * i + st_row;                              // r = tap*BN + co
             const int tap = r / BN, co = r - tap * BN;
             const uint32_t off = ((uint32_t)((tap * C + n0 + co) * C) + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
@@ -152,17 +155,24 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 #pragma unroll
             for (int j = 0; j < 6; ++j)
                 a[j] = *reinterpret_cast<const bf16x8v*>(abuf + (wm * 64 + j * 16) * 64 + rd_off);
+            // (tap, ni) groups of 4 MFMAs; weight fragments are read LA groups ahead.
+            constexpr int NG = 3 * NF, LA = 4;
+            auto bfrag = [&](int gidx) {
+                const int tap = gidx / NF, ni = gidx - tap * NF;
+                return *reinterpret_cast<const bf16x8v*>(bbuf + (tap * BN + wn * 16 * NF + ni * 16) * 64 + rd_off);
+            };
+            bf16x8v bq[LA];
 #pragma unroll
-            for (int tap = 0; tap < 3; ++tap) {
-                bf16x8v b[NF];
+            for (int q = 0; q < LA; ++q)
+                if (q < NG) bq[q] = bfrag(q);
 #pragma unroll
-                for (int ni = 0; ni < NF; ++ni)
-                    b[ni] = *reinterpret_cast<const bf16x8v*>(bbuf + (tap * BN + wn * 16 * NF + ni * 16) * 64 + rd_off);
+            for (int gi = 0; gi < NG; ++gi) {
+                const int tap = gi / NF, ni = gi - tap * NF;
+                const bf16x8v b = bq[gi % LA];
+                if (gi + LA < NG) bq[gi % LA] = bfrag(gi + LA);
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < NF; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ni], a[mi + tap], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[mi + tap], acc[mi][ni], 0, 0, 0);
             }
         }
         // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, location
@@ -228,10 +238,10 @@ __global__ void __launch_bounds__(256) conv3_f32(const float* __restrict__ x, co
 namespace vinf_host {
 using namespace vinf;
 
-template <int NF>
+template <int NF, int WN>
 static vinf_status launch_bf16(const void* x, const void* pre, const void* post, const void* w, const float* bias,
                                void* y, int F, int S, int C, hipStream_t st) {
-    const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP, ntn = C / (32 * NF);
+    const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP, ntn = C / ConvLds<NF, WN>::BN;
     const int64_t tiles = (int64_t)nfb * nlb * ntn;
     if (tiles > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: too many tiles");
     if ((uint64_t)S * C * 2 >= 0x80000000ull || (uint64_t)3 * C * C * 2 >= 0x80000000ull)
@@ -240,7 +250,7 @@ static vinf_status launch_bf16(const void* x, const void* pre, const void* post,
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return fail(VINF_ERR_HIP, "temporal_conv3: cannot query the device");
     const int grid = (int)std::min<int64_t>(cus, tiles);
-    hipLaunchKernelGGL(conv3_bf16<NF>, dim3(grid), dim3(512), 0, st, static_cast<const uint16_t*>(x),
+    hipLaunchKernelGGL((conv3_bf16<NF, WN>), dim3(grid), dim3(256 * WN), 0, st, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(pre), static_cast<const uint16_t*>(post),
                        static_cast<const uint16_t*>(w), bias, static_cast<uint16_t*>(y), F, S, C, nfb, nlb, ntn);
     return VINF_OK;
@@ -251,15 +261,15 @@ vinf_status launch_conv3(const void* x, const void* ctx_pre, const void* ctx_pos
     if (dt == VINF_BF16) {
         vinf_status r;
         if (C % 320 == 0)
-            r = launch_bf16<10>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<5, 4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         else if (C % 256 == 0)
-            r = launch_bf16<8>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<4, 4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         else if (C % 128 == 0)
-            r = launch_bf16<4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<2, 4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         else if (C % 64 == 0)
-            r = launch_bf16<2>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<2, 2>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         else
-            r = launch_bf16<1>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<1, 2>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
         if (r != VINF_OK) return r;
     } else {
         const int64_t n = (int64_t)F * S * C;
