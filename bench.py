@@ -96,7 +96,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--cpu-side", type=int, default=16, help="locations per side of the CPU-baseline sample")
+    ap.add_argument("--cpu-side", type=int, default=32, help="locations per side of the CPU-baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy the input tensor once (a plain device copy of known size, for HBM counters)")
+    ap.add_argument("--no-distinct", action="store_true",
+                    help="skip the attention call on three distinct Q, K, V tensors")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} requested)",
@@ -123,6 +127,9 @@ def main():
     rstd = torch.empty(G, device=dev)
     ws = torch.empty(vinf.groupnorm_workspace_bytes(F, H, W, C, G, x.dtype), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration:
+        g.copy_(x)  # 2 * F*H*W*C bytes of plain HBM traffic, before anything else
+        torch.cuda.synchronize()
 
     def step(ev=None):
         if ev:
@@ -178,6 +185,30 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic_record(dom)}
     roof["ms_per_launch"] = round(mod_ms[dom], 4)
 
+    # Attention on three distinct tensors (in the chain Q, K and V are one
+    # tensor, so that call reads half the bytes a general call must).
+    distinct = None
+    if not args.no_distinct:
+        kd = torch.empty_like(x)
+        vd = torch.empty_like(x)
+        kd.copy_(cv.flip(0))      # frames reversed: different data, same distribution
+        vd.copy_(g)
+        for _ in range(2):
+            vinf.dual_domain_attn(cv, kd, vd, out=o, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            vinf.dual_domain_attn(cv, kd, vd, out=o, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        gbs = work["dda_bf16"]["bytes"] / (ms * 1e-3) / 1e9
+        distinct = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del kd, vd
+        step()  # restore o to the chain's output for the parity check
+        torch.cuda.synchronize()
+
     parity = None
     if not args.no_check:
         import oracle
@@ -209,6 +240,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "dda_bf16_distinct_qkv": distinct,
         "wall_s_timed": wall,
         "parity_sampled": parity,
     }

@@ -134,12 +134,25 @@ __global__ void __launch_bounds__(256) gn_finalize(const float* __restrict__ par
     __shared__ double red[256];
     const int g = blockIdx.x;
     const int64_t items = (int64_t)B * cpg;
-    double s = 0.0;
-    for (int64_t i = threadIdx.x; i < items; i += 256) {
-        int64_t b = i / cpg;
-        int c = g * cpg + (int)(i - b * cpg);
-        s += (double)partial[b * C + c];
+    // item i = (block b = i / cpg, channel g*cpg + i % cpg); thread t owns items
+    // t, t+256, ...; eight loads in flight into eight fp64 partial sums.
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t i = threadIdx.x;
+    for (; i + 7 * 256 < items; i += 8 * 256) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t it = i + u * 256, b = it / cpg;
+            v[u] = partial[b * C + g * cpg + (int)(it - b * cpg)];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += (double)v[u];
     }
+    for (int u = 0; i < items; i += 256, ++u) {
+        const int64_t b = i / cpg;
+        acc[u & 7] += (double)partial[b * C + g * cpg + (int)(i - b * cpg)];
+    }
+    double s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
