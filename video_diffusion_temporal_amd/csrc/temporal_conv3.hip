@@ -25,9 +25,11 @@
 //     one chunk per lane group) free of bank conflicts (measured with the
 //     LDS bank-conflict counter) and makes each lane's slot a constant, so
 //     all fragment reads use immediate offsets.
-//   * 8 waves as 4 (M) x 2 (N); a wave owns 4 frames x 16*NF channels and
-//     reads 6 x fragments (4 frames + the two tap shifts) and 3*NF weight
-//     fragments per slice.  The weight fragment is the MFMA's A operand, so
+//   * 4 (M) x WN (N) waves; a wave owns 4 frames x 16*NF channels and reads
+//     6 x fragments (4 frames + the two tap shifts) and 3*NF weight fragments
+//     per slice, the weight fragments LA groups of 4 MFMAs ahead (pinned
+//     with scheduling-group hints; the compiler otherwise reads them just
+//     before use).  The weight fragment is the MFMA's A operand, so
 //     each lane's accumulator holds 4 consecutive output channels of one
 //     voxel and the epilogue writes 8-byte pieces of channel-contiguous rows.
 //   * Persistent: one 512-thread workgroup per CU walks a contiguous range of
@@ -156,7 +158,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
             for (int j = 0; j < 6; ++j)
                 a[j] = *reinterpret_cast<const bf16x8v*>(abuf + (wm * 64 + j * 16) * 64 + rd_off);
             // (tap, ni) groups of 4 MFMAs; weight fragments are read LA groups ahead.
-            constexpr int NG = 3 * NF, LA = 4;
+            constexpr int NG = 3 * NF, LA = 3;
             auto bfrag = [&](int gidx) {
                 const int tap = gidx / NF, ni = gidx - tap * NF;
                 return *reinterpret_cast<const bf16x8v*>(bbuf + (tap * BN + wn * 16 * NF + ni * 16) * 64 + rd_off);
@@ -173,6 +175,13 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[mi + tap], acc[mi][ni], 0, 0, 0);
+            }
+            // Keep the fragment reads LA groups ahead of their MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, 6 + LA, 0);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                if (gi + LA < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         }
         // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, location
