@@ -44,11 +44,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_conv3.argtypes = [vp, vp, vp, vp, vp, i, i64, i64, i64, vp, i64, vp, i]
         L.oracle_dda_keys.argtypes = [i64, i64, i, i, vp]
         L.oracle_dda.argtypes = [vp, vp, vp, i, i64, i64, i64, i, i, i, d, vp, i64, vp, i]
+        L.oracle_gn_clip_sums.argtypes = [vp, i, i64, i64, i64, i64, vp, vp, i]
+        L.oracle_dda_clip.argtypes = [vp, vp, vp, vp, vp, i, i64, i64, i64, i64, i64, i64, i64, i, i, i, d, vp, i64,
+                                      vp, i]
         L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, vp, i64, vp, vp, vp, vp, vp, vp, vp, i]
         L.oracle_round_to.argtypes = [d, i]
         L.oracle_round_to.restype = d
         for fn in ("oracle_gn_stats", "oracle_groupnorm", "oracle_conv3", "oracle_dda_keys", "oracle_dda",
-                   "oracle_chain"):
+                   "oracle_chain", "oracle_gn_clip_sums", "oracle_dda_clip"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -93,6 +96,19 @@ def gn_stats(x, G, eps=1e-5, nthreads=0):
     if rc:
         raise ValueError(f"oracle_gn_stats rc={rc}")
     return mean, var, rstd
+
+
+def gn_clip_sums(x, G, mean=None, nthreads=0):
+    """sums[G] (fp64) of one clip: of x (mean None) or of (x - mean[g])^2."""
+    x = _c(x)
+    F, S, C = _fsc(x)
+    m = None if mean is None else np.ascontiguousarray(mean, dtype=np.float64)
+    assert m is None or m.size == G
+    sums = np.empty(G)
+    rc = lib().oracle_gn_clip_sums(_ptr(x), _dt(x), F, S, C, G, _ptr(m), _ptr(sums), nthreads)
+    if rc:
+        raise ValueError(f"oracle_gn_clip_sums rc={rc}")
+    return sums
 
 
 def groupnorm(x, G, eps=1e-5, gamma=None, beta=None, locs=None, nthreads=0):
@@ -145,6 +161,28 @@ def dda(q, k, v, head_dim=64, n_local=16, n_global=16, scale=0.0, locs=None, nth
                           _ptr(locs), locs.size, _ptr(o), nthreads)
     if rc:
         raise ValueError(f"oracle_dda rc={rc}")
+    return o
+
+
+def dda_clip(q, k, v, F_total, f0, kf0, k_glob=None, v_glob=None, head_dim=64, n_local=16, n_global=16,
+             scale=0.0, locs=None, nthreads=0):
+    """o[Fc, n_locs, C] for query frames f0 .. f0+Fc-1 of an F_total-frame video.
+
+    q is [Fc, ...]; k, v hold frames kf0 .. kf0+len(k)-1; k_glob, v_glob hold
+    the global frames floor(i*F_total/n_global) (None: read from k, v)."""
+    q, k, v, kg, vg = _c(q), _c(k), _c(v), _c(k_glob), _c(v_glob)
+    Fc, S, C = _fsc(q)
+    n_ext = _fsc(k)[0]
+    assert k.shape == v.shape and k.dtype == v.dtype == q.dtype and _fsc(k)[1:] == (S, C)
+    assert (kg is None) == (vg is None)
+    if kg is not None:
+        assert kg.shape == vg.shape and _fsc(kg) == (n_global, S, C) and kg.dtype == q.dtype == vg.dtype
+    locs = _locs(locs, S)
+    o = np.empty((Fc, locs.size, C))
+    rc = lib().oracle_dda_clip(_ptr(q), _ptr(k), _ptr(v), _ptr(kg), _ptr(vg), _dt(q), F_total, f0, Fc, kf0, n_ext,
+                               S, C, head_dim, n_local, n_global, scale, _ptr(locs), locs.size, _ptr(o), nthreads)
+    if rc:
+        raise ValueError(f"oracle_dda_clip rc={rc}")
     return o
 
 

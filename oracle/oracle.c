@@ -144,6 +144,26 @@ int oracle_gn_stats(const void* x, int dt, int64_t F, int64_t S, int64_t C, int6
     return 0;
 }
 
+/* One clip's share of the two sums (the per-device step before the
+ * aggregation across devices): sums[g] = sum over the clip's voxels of x
+ * (mean == NULL) or of (x - mean[g])^2. */
+int oracle_gn_clip_sums(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, const double* mean,
+                        double* sums, int nthreads) {
+    if (!x || !sums || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || G < 1 || C % G) return 1;
+    nthreads = resolve_threads(nthreads);
+    double* partial = (double*)calloc((size_t)nthreads * (size_t)G, sizeof(double));
+    if (!partial) return 2;
+    gn_ctx c = {x, dt, C, G, C / G, mean, partial};
+    parallel_ranges(F * S, nthreads, gn_pass, &c);
+    for (int64_t g = 0; g < G; ++g) {
+        double s = 0.0;
+        for (int t = 0; t < nthreads; ++t) s += partial[(int64_t)t * G + g];
+        sums[g] = s;
+    }
+    free(partial);
+    return 0;
+}
+
 int oracle_groupnorm(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, double eps,
                      const double* gamma, const double* beta, const int64_t* locs, int64_t n_locs,
                      double* y, double* mean, double* rstd, int nthreads) {
@@ -266,37 +286,52 @@ int oracle_dda_keys(int64_t F, int64_t t, int n_local, int n_global, int64_t* ke
     return n;
 }
 
+/* The video is F frames long; the query frames are f0 .. f0+Fc-1 (q and o
+ * row 0 is frame f0); k and v hold the n_ext frames kf0 .. kf0+n_ext-1 (row 0
+ * is frame kf0).  The global rows come from kg, vg (row i holds frame
+ * floor(i*F/Gk)) or, when those are NULL, from k and v themselves.  The whole
+ * video is the case f0 = kf0 = 0, Fc = n_ext = F, kg = vg = NULL. */
 typedef struct {
-    const void *q, *k, *v;
+    const void *q, *k, *v, *kg, *vg;
     int dt;
-    int64_t F, S, C, n_locs;
+    int64_t F, f0, Fc, kf0, n_ext, S, C, n_locs;
     int dh, L, Gk;
     double scale;
     const int64_t* locs;
     double* o;
 } dda_ctx;
 
+/* Element (row of key j, location s, channel ch) of k (want_v = 0) or v. */
+static double dda_kv(const dda_ctx* c, int want_v, const int64_t* keys, int nl, int j, int64_t s, int64_t ch) {
+    const void* ext = want_v ? c->v : c->k;
+    const void* glob = want_v ? c->vg : c->kg;
+    int64_t row = (j >= nl && glob) ? (int64_t)(j - nl) : keys[j] - c->kf0;
+    const void* base = (j >= nl && glob) ? glob : ext;
+    return load(base, c->dt, (row * c->S + s) * c->C + ch);
+}
+
 static void dda_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
     (void)tid;
     dda_ctx* c = (dda_ctx*)vctx;
-    int64_t F = c->F, S = c->S, C = c->C;
+    int64_t S = c->S, C = c->C;
     int nmax = c->L + c->Gk;
     int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)nmax);
     double* sc = (double*)malloc(sizeof(double) * (size_t)nmax);
     double* acc = (double*)malloc(sizeof(double) * (size_t)c->dh);
     if (!keys || !sc || !acc) abort();
+    const int nl = (int)(c->L < c->F ? c->L : c->F);
     for (int64_t li = l0; li < l1; ++li) {
         int64_t s = c->locs[li];
         for (int64_t h = 0; h < C / c->dh; ++h) {
             int64_t c0 = h * c->dh;
-            for (int64_t t = 0; t < F; ++t) {
-                int n = oracle_dda_keys(F, t, c->L, c->Gk, keys);
+            for (int64_t i = 0; i < c->Fc; ++i) {
+                int64_t t = c->f0 + i;
+                int n = oracle_dda_keys(c->F, t, c->L, c->Gk, keys);
                 double m = -INFINITY;
                 for (int j = 0; j < n; ++j) {
                     double d = 0.0;
                     for (int e = 0; e < c->dh; ++e)
-                        d += load(c->q, c->dt, (t * S + s) * C + c0 + e) *
-                             load(c->k, c->dt, (keys[j] * S + s) * C + c0 + e);
+                        d += load(c->q, c->dt, (i * S + s) * C + c0 + e) * dda_kv(c, 0, keys, nl, j, s, c0 + e);
                     sc[j] = c->scale * d;
                     if (sc[j] > m) m = sc[j];
                 }
@@ -305,9 +340,9 @@ static void dda_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
                 for (int j = 0; j < n; ++j) {
                     double p = exp(sc[j] - m);
                     den += p;
-                    for (int e = 0; e < c->dh; ++e) acc[e] += p * load(c->v, c->dt, (keys[j] * S + s) * C + c0 + e);
+                    for (int e = 0; e < c->dh; ++e) acc[e] += p * dda_kv(c, 1, keys, nl, j, s, c0 + e);
                 }
-                for (int e = 0; e < c->dh; ++e) c->o[(t * c->n_locs + li) * C + c0 + e] = acc[e] / den;
+                for (int e = 0; e < c->dh; ++e) c->o[(i * c->n_locs + li) * C + c0 + e] = acc[e] / den;
             }
         }
     }
@@ -316,20 +351,50 @@ static void dda_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
     free(acc);
 }
 
+static int dda_run(dda_ctx* c, int nthreads) {
+    if (!c->q || !c->k || !c->v || !c->o || !c->locs || (c->dt != 0 && c->dt != 1) || c->F < 1 || c->S < 1 ||
+        c->C < 1 || c->dh < 1 || c->C % c->dh || c->L < 0 || c->Gk < 0 || c->L + c->Gk < 1 || c->n_locs < 0 ||
+        (!c->kg) != (!c->vg))
+        return 1;
+    if (c->f0 < 0 || c->Fc < 1 || c->f0 + c->Fc > c->F || c->kf0 < 0 || c->n_ext < 1 || c->kf0 + c->n_ext > c->F)
+        return 1;
+    for (int64_t i = 0; i < c->n_locs; ++i)
+        if (c->locs[i] < 0 || c->locs[i] >= c->S) return 1;
+    /* every key row read from k and v must be one of their n_ext frames */
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(c->L + c->Gk));
+    if (!keys) return 2;
+    const int64_t nl = c->L < c->F ? c->L : c->F;
+    int missing = 0;
+    for (int64_t t = c->f0; t < c->f0 + c->Fc && !missing; ++t) {
+        int n = oracle_dda_keys(c->F, t, c->L, c->Gk, keys);
+        for (int j = 0; j < n; ++j) {
+            if (j >= nl && c->kg) continue;
+            if (keys[j] < c->kf0 || keys[j] >= c->kf0 + c->n_ext) missing = 1;
+        }
+    }
+    free(keys);
+    if (missing) return 3;
+    if (c->scale <= 0.0) c->scale = 1.0 / sqrt((double)c->dh);
+    nthreads = resolve_threads(nthreads);
+    if (nthreads > c->n_locs) nthreads = c->n_locs > 0 ? (int)c->n_locs : 1;
+    parallel_ranges(c->n_locs, nthreads, dda_locs, c);
+    return 0;
+}
+
 int oracle_dda(const void* q, const void* k, const void* v, int dt, int64_t F, int64_t S, int64_t C,
                int head_dim, int n_local, int n_global, double scale, const int64_t* locs,
                int64_t n_locs, double* o, int nthreads) {
-    if (!q || !k || !v || !o || !locs || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || head_dim < 1 ||
-        C % head_dim || n_local < 0 || n_global < 0 || n_local + n_global < 1 || n_locs < 0)
-        return 1;
-    for (int64_t i = 0; i < n_locs; ++i)
-        if (locs[i] < 0 || locs[i] >= S) return 1;
-    if (scale <= 0.0) scale = 1.0 / sqrt((double)head_dim);
-    nthreads = resolve_threads(nthreads);
-    if (nthreads > n_locs) nthreads = n_locs > 0 ? (int)n_locs : 1;
-    dda_ctx c = {q, k, v, dt, F, S, C, n_locs, head_dim, n_local, n_global, scale, locs, o};
-    parallel_ranges(n_locs, nthreads, dda_locs, &c);
-    return 0;
+    dda_ctx c = {q, k, v, NULL, NULL, dt, F, 0, F, 0, F, S, C, n_locs, head_dim, n_local, n_global, scale, locs, o};
+    return dda_run(&c, nthreads);
+}
+
+int oracle_dda_clip(const void* q, const void* k, const void* v, const void* k_glob, const void* v_glob, int dt,
+                    int64_t F_total, int64_t f0, int64_t Fc, int64_t kf0, int64_t n_ext, int64_t S, int64_t C,
+                    int head_dim, int n_local, int n_global, double scale, const int64_t* locs, int64_t n_locs,
+                    double* o, int nthreads) {
+    dda_ctx c = {q, k, v, k_glob, v_glob, dt, F_total, f0, Fc, kf0, n_ext, S, C, n_locs,
+                 head_dim, n_local, n_global, scale, locs, o};
+    return dda_run(&c, nthreads);
 }
 
 /* ---- The three modules in a row --------------------------------------- */

@@ -15,7 +15,11 @@
  *     sets both context sizes to 16 (local neighbour frames + frames sampled
  *     uniformly over the whole video);
  *   - oracle_chain: the three temporal modules in a row (the paragraph that
- *     lists Attention, Conv and GroupNorm as the temporal modules).
+ *     lists Attention, Conv and GroupNorm as the temporal modules);
+ *   - oracle_gn_clip_sums / oracle_dda_clip: the clip-parallel form (the
+ *     clip-parallelism paragraph: each device's temporal module maps its clip
+ *     plus context from the previous clip, the next clip and a global context
+ *     to its output), with the GroupNorm and attention paragraphs above.
  * Readings of points the page leaves open are stated at each function.
  *
  * Tensors are dense channels-last [F][S][C] (S = H*W spatial locations), given
@@ -47,6 +51,13 @@ int oracle_groupnorm(const void* x, int dt, int64_t F, int64_t S, int64_t C, int
                      const double* gamma, const double* beta, const int64_t* locs, int64_t n_locs,
                      double* y, double* mean, double* rstd, int nthreads);
 
+/* One clip's share of the GroupNorm sums: sums[g] = sum of x over the clip's
+ * F*S voxels and group g's channels (mean == NULL, first pass), or of
+ * (x - mean[g])^2 (second pass, mean = the global means).  Summed over all
+ * clips and divided by the whole video's N_g they give mean_g and var_g. */
+int oracle_gn_clip_sums(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, const double* mean,
+                        double* sums, int nthreads);
+
 /* y[f,s,co] = bias[co] + sum_{k=0..2} sum_ci w[k][co][ci] * xt[f+k-1, s, ci],
  * xt[-1] = ctx_pre (or 0 if NULL), xt[F] = ctx_post (or 0 if NULL).
  * w is [3][C][C] in dt; ctx_* are [S][C] in dt; bias is [C] double or NULL. */
@@ -66,6 +77,19 @@ int oracle_dda_keys(int64_t F, int64_t t, int n_local, int n_global, int64_t* ke
 int oracle_dda(const void* q, const void* k, const void* v, int dt, int64_t F, int64_t S, int64_t C,
                int head_dim, int n_local, int n_global, double scale, const int64_t* locs,
                int64_t n_locs, double* o, int nthreads);
+
+/* Attention of one clip of an F_total-frame video (the clip-parallel form of
+ * the temporal module: a clip's frames plus context taken from the others).
+ * Query frames f0 .. f0+Fc-1; q and o are [Fc][S][C] / [Fc][n_locs][C].
+ * k and v are [n_ext][S][C] holding frames kf0 .. kf0+n_ext-1.  k_glob and
+ * v_glob are [n_global][S][C] holding frames floor(i*F_total/n_global), or
+ * both NULL: the global rows are then read from k and v.  The key multiset is
+ * oracle_dda_keys(F_total, t, ...).  Returns 3 when a key frame read from k/v
+ * is not among their frames. */
+int oracle_dda_clip(const void* q, const void* k, const void* v, const void* k_glob, const void* v_glob, int dt,
+                    int64_t F_total, int64_t f0, int64_t Fc, int64_t kf0, int64_t n_ext, int64_t S, int64_t C,
+                    int head_dim, int n_local, int n_global, double scale, const int64_t* locs, int64_t n_locs,
+                    double* o, int nthreads);
 
 /* GroupNorm (identity affine) -> round to dt -> conv3 (zero padded, no bias)
  * -> round to dt -> dual-domain attention with Q = K = V = the conv output.
