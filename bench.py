@@ -89,6 +89,85 @@ def cpu_baseline(F, C, G, side=16):
             "seconds": dt}
 
 
+def timed(fn, steps, stream):
+    """Average ms of fn() over `steps` calls (HIP events on the launch stream)."""
+    import torch
+
+    for _ in range(2):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def hbm_entry(ms, nbytes):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+
+
+def next_rows(vinf, x, cv, gn, G, stream, steps, work):
+    """The clip-parallel forms and the attention ablations, each timed alone.
+
+    Clip form: one of eight clips of a 2300-frame video (frames 864..1151,
+    288 frames) at the same 64x40x320 bf16 locations, with its 8 + 7 context
+    frames and the 16 gathered global rows, as one device of an 8-way clip
+    split would run it.  Ablations: the local-only and global-only key sets at
+    F=1024 on the chain's conv output (Q = K = V)."""
+    import torch
+
+    F, H, W, C = x.shape
+    S, b = H * W, 2
+    out = {}
+    # attention of a clip, distinct Q/K/V (a device's projections are three tensors)
+    F_total, f0, Fc = 2300, 864, 288
+    pre, post = vinf.dda_clip_halo(F_total, f0, Fc)
+    n_ext = pre + Fc + post
+    q = cv[:Fc]
+    k = gn[:n_ext]
+    v = torch.empty((n_ext, H, W, C), device=x.device, dtype=x.dtype)
+    v.copy_(cv[F - n_ext:].flip(0))
+    kg = torch.empty((16, H, W, C), device=x.device, dtype=x.dtype)
+    vg = torch.empty_like(kg)
+    kg.copy_(x[:16])
+    vg.copy_(x[16:32])
+    o = torch.empty_like(q)
+    ms = timed(lambda: vinf.dual_domain_attn_clip(q, k, v, F_total, f0, pre, post, kg, vg, out=o, stream=stream),
+               steps, stream)
+    out["dda_bf16_clip"] = dict(hbm_entry(ms, S * C * b * (2 * Fc + 2 * n_ext + 32)),
+                                shape=f"clip [{f0},{f0 + Fc}) of {F_total} frames, context {pre}+{post}, "
+                                      f"{H}x{W}x{C}, distinct q/k/v, external global rows")
+    del q, k, v, kg, vg, o
+    # ablations on the chain's tensor (Q = K = V): the same bytes as the chain call less the global rows
+    o = torch.empty_like(cv)
+    for name, nl, ng, nbytes in (("dda_bf16_local_only", 16, 0, F * S * 4 * C * b),
+                                 ("dda_bf16_global_only", 0, 16, F * S * 2 * C * b + S * 32 * C * b)):
+        ms = timed(lambda: vinf.dual_domain_attn(cv, cv, cv, out=o, n_local=nl, n_global=ng, stream=stream), steps,
+                   stream)
+        out[name] = dict(hbm_entry(ms, nbytes), shape=f"F={F}, {H}x{W}x{C}, Q = K = V (n_local={nl}, n_global={ng})")
+    del o
+    # GroupNorm of one clip (288 frames): two sum sweeps and the apply
+    xc = x[:Fc]
+    yc = torch.empty_like(xc)
+    ws = torch.empty(vinf.groupnorm_workspace_bytes(Fc, H, W, C, G, x.dtype), device=x.device, dtype=torch.uint8)
+    s1 = torch.empty(G, device=x.device, dtype=torch.float64)
+    s2 = torch.empty_like(s1)
+
+    def gn_clip():
+        vinf.groupnorm_clip_sums(xc, G, F_total, out=s1, workspace=ws, stream=stream)
+        vinf.groupnorm_clip_sums(xc, G, F_total, s1, out=s2, workspace=ws, stream=stream)
+        vinf.groupnorm_clip_apply(xc, G, F_total, s1, s2, out=yc, workspace=ws, stream=stream)
+
+    ms = timed(gn_clip, steps, stream)
+    out["groupnorm_clip"] = dict(hbm_entry(ms, Fc * S * 4 * C * b),
+                                 shape=f"clip of {Fc} frames, {H}x{W}x{C}, groups={G} (sums, sums, apply)")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +180,8 @@ def main():
                     help="first copy the input tensor once (a plain device copy of known size, for HBM counters)")
     ap.add_argument("--no-distinct", action="store_true",
                     help="skip the attention call on three distinct Q, K, V tensors")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the clip-form and ablation measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} requested)",
@@ -209,6 +290,8 @@ def main():
         step()  # restore o to the chain's output for the parity check
         torch.cuda.synchronize()
 
+    nxt = None if args.no_next else next_rows(vinf, x, cv, g, G, stream, args.steps, work)
+
     parity = None
     if not args.no_check:
         import oracle
@@ -241,6 +324,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "dda_bf16_distinct_qkv": distinct,
+        "next_rows": nxt,
         "wall_s_timed": wall,
         "parity_sampled": parity,
     }

@@ -92,7 +92,10 @@ vinf_status vinf_groupnorm_global(const void* x, void* y, const float* gamma, co
  *   xt[-1] = ctx_pre, xt[F] = ctx_post (zeros when NULL: the ends of the video)
  *
  * x, y      [F][H][W][C] in dt; y must not overlap x, weight or ctx_*.
- * ctx_pre, ctx_post  [H][W][C] in dt, or NULL.
+ * ctx_pre, ctx_post  [H][W][C] in dt, or NULL.  For a clip of a longer
+ *           video they are the previous clip's last frame and the next clip's
+ *           first frame; the clip's y then equals the whole video's y for
+ *           those frames, bit for bit.
  * weight    [3][C_out=C][C_in=C] in dt (tap k multiplies frame f+k-1; a torch
  *           Conv1d weight [C_out][C_in][3] maps to it by permute(2,0,1)).
  * bias      [C] float32 or NULL.
@@ -121,13 +124,85 @@ vinf_status vinf_temporal_conv3(const void* x, const void* ctx_pre, const void* 
  * o         [F][H][W][C] in dt, before any output projection; must not
  *           overlap q, k or v.
  * scale     <= 0 selects 1/sqrt(head_dim).
- * Limits    head_dim == 64, C % 64 == 0, n_local == 16 and n_global == 16
- *           (anything else: VINF_ERR_UNSUPPORTED).  F >= 1 (F < 16 uses all
- *           F frames as the local context).
+ * Limits    head_dim == 64, C % 64 == 0; n_local and n_global each 16 or 0,
+ *           not both 0 (anything else: VINF_ERR_UNSUPPORTED).  F >= 1 (F < 16
+ *           uses all F frames as the local context).
+ *           n_global == 0 is the local-context-only variant and n_local == 0
+ *           the global-context-only variant of the write-up's ablation
+ *           paragraph (the key list is then just the other half).
  */
 vinf_status vinf_dual_domain_attn(const void* q, const void* k, const void* v, void* o, int F, int H,
                                   int W, int C, int head_dim, int n_local, int n_global, float scale,
                                   vinf_dtype dt, vinf_stream stream);
+
+/*
+ * GroupNorm of one clip with statistics over the whole video (the clip-
+ * parallelism paragraph: each device holds a clip and its temporal modules
+ * exchange context; for GroupNorm the context is the aggregated statistics
+ * of the GroupNorm-module paragraph).  Per clip, in this order:
+ *
+ *   1. vinf_groupnorm_clip_sums(x, NULL, s1)  s1[g] = sum of x over the clip
+ *   2. caller: S1 = sum of s1 over all clips (e.g. an fp64 all-reduce)
+ *   3. vinf_groupnorm_clip_sums(x, S1, s2)   s2[g] = sum of (x - mean_g)^2,
+ *                                             mean_g = S1[g] / N_g
+ *   4. caller: S2 = sum of s2 over all clips
+ *   5. vinf_groupnorm_clip_apply(x, y, ..., S1, S2)
+ *        y = (x - mean_g) / sqrt(S2[g]/N_g + eps) * gamma_c + beta_c
+ *
+ *   N_g = F_total*H*W*C/groups, F_total = the frames of all clips together.
+ *
+ * x, y      [F][H][W][C] in dt: this clip's F frames (y == x allowed).
+ * mean_sums, sums, sq_sums  [groups] float64 device arrays (8-byte aligned);
+ *           mean_sums NULL selects step 1.  sums must not overlap x, the
+ *           workspace or mean_sums.
+ * gamma, beta, mean_out, rstd_out, eps, workspace: as vinf_groupnorm_global,
+ *           with the workspace sized by vinf_groupnorm_workspace_bytes for
+ *           this clip's F.
+ * The sums and statistics use the same kernels and expressions as
+ * vinf_groupnorm_global, so a single clip with F_total == F gives the same
+ * bits as that call.
+ */
+vinf_status vinf_groupnorm_clip_sums(const void* x, const double* mean_sums, double* sums, int F, int H, int W,
+                                     int C, int groups, int F_total, vinf_dtype dt, void* workspace,
+                                     size_t workspace_bytes, vinf_stream stream);
+vinf_status vinf_groupnorm_clip_apply(const void* x, void* y, const float* gamma, const float* beta,
+                                      const double* sums, const double* sq_sums, float* mean_out,
+                                      float* rstd_out, int F, int H, int W, int C, int groups, int F_total,
+                                      float eps, vinf_dtype dt, void* workspace, size_t workspace_bytes,
+                                      vinf_stream stream);
+
+/*
+ * Context a clip needs for the local keys of its queries: the clip holds
+ * frames f0 .. f0+Fc-1 of an F_total-frame video; *n_pre / *n_post receive
+ * how many frames before f0 and after f0+Fc-1 its local windows reach
+ * (8 and 7 for an interior clip of >= 16 frames; up to 15 next to the ends
+ * of the video, where windows shift inward; 0 and 0 when n_local == 0).
+ * Host only: touches no device state.
+ */
+vinf_status vinf_dda_clip_halo(int F_total, int f0, int Fc, int n_local, int* n_pre, int* n_post);
+
+/*
+ * Dual-domain attention of one clip (the clip-parallel form: the clip's own
+ * frames plus the previous clip's and next clip's edge frames as local
+ * context and the global context frames gathered from all clips).  Computes
+ * vinf_dual_domain_attn of the whole video restricted to query frames
+ * f0 .. f0+Fc-1, bit for bit, from:
+ *
+ * q, o      [Fc][H][W][C] in dt (frames f0 .. f0+Fc-1).
+ * k, v      [n_pre + Fc + n_post][H][W][C] in dt: frames f0-n_pre ..
+ *           f0+Fc+n_post-1, the clip's rows with the neighbours' rows in
+ *           place before and after.  n_pre / n_post must be at least what
+ *           vinf_dda_clip_halo reports, and the frames must lie in the video.
+ * k_global, v_global  [n_global][H][W][C] in dt: frames floor(i*F_total/16),
+ *           i = 0..15, of the video's K and V; or both NULL, when k and v
+ *           hold all of those frames (e.g. the whole video).
+ * Other arguments, limits and errors as vinf_dual_domain_attn.  o must not
+ *           overlap any input.
+ */
+vinf_status vinf_dual_domain_attn_clip(const void* q, const void* k, const void* v, const void* k_global,
+                                       const void* v_global, void* o, int F_total, int f0, int Fc, int n_pre,
+                                       int n_post, int H, int W, int C, int head_dim, int n_local,
+                                       int n_global, float scale, vinf_dtype dt, vinf_stream stream);
 
 /* Static description of a status code. */
 const char* vinf_status_string(vinf_status s);

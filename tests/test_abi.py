@@ -34,7 +34,9 @@ def test_library_is_built_and_loads():
 def test_exports_every_declared_function():
     names = declared_functions()
     assert set(names) >= {"vinf_groupnorm_global", "vinf_temporal_conv3", "vinf_dual_domain_attn",
-                          "vinf_groupnorm_workspace_bytes", "vinf_status_string", "vinf_last_error"}
+                          "vinf_groupnorm_workspace_bytes", "vinf_status_string", "vinf_last_error",
+                          "vinf_groupnorm_clip_sums", "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo",
+                          "vinf_dual_domain_attn_clip"}
     lib = ctypes.CDLL(vinf.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -73,6 +75,7 @@ def attn(**kw):
     (dict(F=0), INVALID), (dict(H=-1), INVALID), (dict(W=0), INVALID), (dict(C=0), INVALID),
     (dict(C=96), INVALID),                       # not a multiple of head_dim
     (dict(hd=32, C=64), UNSUPPORTED), (dict(nl=8), UNSUPPORTED), (dict(ng=32), UNSUPPORTED),
+    (dict(nl=0, ng=0), UNSUPPORTED), (dict(nl=-16), UNSUPPORTED),
     (dict(C=68), UNSUPPORTED),                   # not a multiple of 8 (bf16 vectors)
     (dict(dt=7), INVALID),
     (dict(o=A), INVALID), (dict(o=B + 256), INVALID),  # o overlaps q / k
@@ -138,3 +141,96 @@ def test_python_binding_requires_gpu_tensors():
         vinf.temporal_conv3(x, torch.zeros(3, 64, 64))
     with pytest.raises(TypeError):
         vinf.groupnorm_global(x, 8)
+
+
+# ------------------------------------------------------------ clip forms
+
+def test_clip_halo_matches_the_key_frames():
+    # Brute force over the oracle's key lists: the first and last local key of
+    # the clip's queries.
+    import oracle
+    for F in (1, 5, 15, 16, 17, 40, 300):
+        for f0 in range(0, F, max(1, F // 7)):
+            for Fc in sorted({1, 2, 7, 16, 33, F - f0}):
+                if Fc < 1 or f0 + Fc > F:
+                    continue
+                keys = [j for t in range(f0, f0 + Fc) for j in oracle.dda_keys(F, t, 16, 0)]
+                assert vinf.dda_clip_halo(F, f0, Fc) == (f0 - min(keys), max(0, max(keys) + 1 - (f0 + Fc))), \
+                    (F, f0, Fc)
+                assert vinf.dda_clip_halo(F, f0, Fc, 0) == (0, 0)
+    assert vinf.dda_clip_halo(2300, 864, 288) == (8, 7)
+
+
+@pytest.mark.parametrize("args", [(0, 0, 1, 16), (10, 5, 6, 16), (10, -1, 2, 16), (10, 0, 0, 16), (10, 0, 2, -1)])
+def test_clip_halo_rejects(args):
+    with pytest.raises(vinf.VinfError):
+        vinf.dda_clip_halo(*args)
+
+
+def attn_clip(**kw):
+    # F_total=100, clip [40, 60) with the minimal context 8 / 7
+    a = dict(q=A, k=B, v=Cp, kg=D, vg=E, o=Fp, Ft=100, f0=40, Fc=20, pre=8, post=7, H=8, W=5, C=64, hd=64, nl=16,
+             ng=16, scale=0.0, dt=BF16)
+    a.update(kw)
+    return vinf.load().vinf_dual_domain_attn_clip(a["q"], a["k"], a["v"], a["kg"], a["vg"], a["o"], a["Ft"], a["f0"],
+                                                  a["Fc"], a["pre"], a["post"], a["H"], a["W"], a["C"], a["hd"],
+                                                  a["nl"], a["ng"], a["scale"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(o=None), INVALID), (dict(kg=D + 8), INVALID),
+    (dict(kg=None), INVALID),                     # one of k_global / v_global
+    (dict(kg=None, vg=None), INVALID),            # global frames not inside k/v
+    (dict(pre=7), INVALID), (dict(post=6), INVALID),   # context shorter than the windows reach
+    (dict(f0=90, Fc=20), INVALID), (dict(f0=-1), INVALID), (dict(Fc=0), INVALID),
+    (dict(f0=5, pre=8), INVALID),                 # context before frame 0
+    (dict(f0=90, Fc=5, post=7), INVALID),         # context past the last frame
+    (dict(pre=-1), INVALID),
+    (dict(nl=8), UNSUPPORTED), (dict(nl=0, ng=0), UNSUPPORTED), (dict(hd=32), UNSUPPORTED),
+    (dict(o=B + 64), INVALID), (dict(o=D), INVALID),   # o overlaps k / k_global
+    (dict(scale=float("nan")), INVALID), (dict(dt=5), INVALID),
+])
+def test_attention_clip_rejects(kw, status):
+    assert attn_clip(**kw) == status
+    assert vinf.load().vinf_last_error()
+
+
+def gn_clip_sums(**kw):
+    L = vinf.load()
+    a = dict(x=A, ms=None, sums=B, F=16, H=8, W=5, C=64, G=8, Ft=64, dt=F32, ws=Cp, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = L.vinf_groupnorm_workspace_bytes(16, 8, 5, 64, 8, F32)
+    return L.vinf_groupnorm_clip_sums(a["x"], a["ms"], a["sums"], a["F"], a["H"], a["W"], a["C"], a["G"], a["Ft"],
+                                      a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(sums=None), INVALID), (dict(sums=B + 4), INVALID), (dict(ms=D + 4), INVALID),
+    (dict(Ft=15), INVALID), (dict(G=7), INVALID), (dict(F=0), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=8), WORKSPACE),
+    (dict(sums=A + 256), INVALID), (dict(ms=B), INVALID),   # sums inside x / equal to mean_sums
+])
+def test_groupnorm_clip_sums_rejects(kw, status):
+    assert gn_clip_sums(**kw) == status
+
+
+def gn_clip_apply(**kw):
+    L = vinf.load()
+    a = dict(x=A, y=B, gamma=None, beta=None, s1=D, s2=E, mean=None, rstd=None, F=16, H=8, W=5, C=64, G=8, Ft=64,
+             eps=1e-5, dt=F32, ws=Cp, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = L.vinf_groupnorm_workspace_bytes(16, 8, 5, 64, 8, F32)
+    return L.vinf_groupnorm_clip_apply(a["x"], a["y"], a["gamma"], a["beta"], a["s1"], a["s2"], a["mean"], a["rstd"],
+                                       a["F"], a["H"], a["W"], a["C"], a["G"], a["Ft"], a["eps"], a["dt"], a["ws"],
+                                       a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(y=None), INVALID), (dict(s1=None), INVALID), (dict(s2=None), INVALID), (dict(s2=E + 2), INVALID),
+    (dict(Ft=3), INVALID), (dict(eps=-1.0), INVALID), (dict(y=A + 16), INVALID), (dict(mean=B + 64), INVALID),
+    (dict(wsb=16), WORKSPACE),
+])
+def test_groupnorm_clip_apply_rejects(kw, status):
+    assert gn_clip_apply(**kw) == status

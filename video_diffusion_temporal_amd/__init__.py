@@ -8,6 +8,13 @@ Call names match the C ABI in include/vinf.h:
     temporal_conv3(x, weight, ctx_pre=None, ...)     -> y
     dual_domain_attn(q, k, v, ...)                   -> o
 
+and the clip-parallel forms (one clip of a longer video plus its context):
+
+    groupnorm_clip_sums(x, groups, F_total, mean_sums=None)  -> sums (float64 [groups])
+    groupnorm_clip_apply(x, groups, F_total, sums, sq_sums)  -> (y, mean, rstd)
+    dda_clip_halo(F_total, f0, Fc, n_local=16)               -> (n_pre, n_post)
+    dual_domain_attn_clip(q, k, v, F_total, f0, n_pre, n_post, k_global, v_global) -> o
+
 Tensors are CUDA (HIP) tensors, contiguous, channels-last [F, H, W, C],
 float32 or bfloat16.  There is no CPU fallback: without the built library
 every call raises.
@@ -19,7 +26,8 @@ import os
 
 import torch
 
-__all__ = ["groupnorm_global", "groupnorm_workspace_bytes", "temporal_conv3", "dual_domain_attn", "VinfError",
+__all__ = ["groupnorm_global", "groupnorm_workspace_bytes", "temporal_conv3", "dual_domain_attn",
+           "groupnorm_clip_sums", "groupnorm_clip_apply", "dda_clip_halo", "dual_domain_attn_clip", "VinfError",
            "library_path", "load", "VINF_F32", "VINF_BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -50,7 +58,12 @@ def load() -> ctypes.CDLL:
         L.vinf_groupnorm_global.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         L.vinf_temporal_conv3.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
         L.vinf_dual_domain_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
-        for fn in ("vinf_groupnorm_global", "vinf_temporal_conv3", "vinf_dual_domain_attn"):
+        L.vinf_groupnorm_clip_sums.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+        L.vinf_groupnorm_clip_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+        L.vinf_dda_clip_halo.argtypes = [i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.vinf_dual_domain_attn_clip.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, f, i, vp]
+        for fn in ("vinf_groupnorm_global", "vinf_temporal_conv3", "vinf_dual_domain_attn", "vinf_groupnorm_clip_sums",
+                   "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo", "vinf_dual_domain_attn_clip"):
             getattr(L, fn).restype = ctypes.c_int
         L.vinf_status_string.argtypes = [i]
         L.vinf_status_string.restype = ctypes.c_char_p
@@ -159,4 +172,94 @@ def dual_domain_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
     st = load().vinf_dual_domain_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), F, H, W, C, head_dim, n_local, n_global,
                                        float(scale), _dtype_code(q), _stream(q.device, stream))
     _check("vinf_dual_domain_attn", st)
+    return o
+
+
+def _workspace(x: torch.Tensor, groups: int, workspace):
+    F, H, W, C = _fhwc(x)
+    need = groupnorm_workspace_bytes(F, H, W, C, groups, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _f64(t: torch.Tensor | None, name: str, groups: int):
+    if t is None:
+        return None
+    _dev(t, name)
+    if t.dtype != torch.float64 or t.numel() != groups:
+        raise ValueError(f"{name} must be float64 [{groups}]")
+    return t
+
+
+def groupnorm_clip_sums(x: torch.Tensor, groups: int, F_total: int, mean_sums: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """One clip's float64 group sums: of x (mean_sums None) or of (x - mean)^2
+    with mean = mean_sums / N_g, where mean_sums holds the first sums of all
+    clips added together and N_g counts the whole video's F_total frames."""
+    _dev(x, "x")
+    F, H, W, C = _fhwc(x)
+    _f64(mean_sums, "mean_sums", groups)
+    sums = torch.empty(groups, device=x.device, dtype=torch.float64) if out is None else _f64(out, "out", groups)
+    workspace, ws_bytes = _workspace(x, groups, workspace)
+    st = load().vinf_groupnorm_clip_sums(_ptr(x), _ptr(mean_sums), _ptr(sums), F, H, W, C, groups, int(F_total),
+                                          _dtype_code(x), _ptr(workspace), ws_bytes, _stream(x.device, stream))
+    _check("vinf_groupnorm_clip_sums", st)
+    return sums
+
+
+def groupnorm_clip_apply(x: torch.Tensor, groups: int, F_total: int, sums: torch.Tensor, sq_sums: torch.Tensor,
+                         eps: float = 1e-5, gamma: torch.Tensor | None = None, beta: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None, mean_out: torch.Tensor | None = None,
+                         rstd_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Normalise one clip with the statistics of the all-clip sums.  Returns (y, mean, rstd)."""
+    _dev(x, "x")
+    F, H, W, C = _fhwc(x)
+    _f64(sums, "sums", groups)
+    _f64(sq_sums, "sq_sums", groups)
+    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    mean = torch.empty(groups, device=x.device, dtype=torch.float32) if mean_out is None else mean_out
+    rstd = torch.empty(groups, device=x.device, dtype=torch.float32) if rstd_out is None else rstd_out
+    workspace, ws_bytes = _workspace(x, groups, workspace)
+    st = load().vinf_groupnorm_clip_apply(_ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(sums), _ptr(sq_sums),
+                                           _ptr(mean), _ptr(rstd), F, H, W, C, groups, int(F_total), float(eps),
+                                           _dtype_code(x), _ptr(workspace), ws_bytes, _stream(x.device, stream))
+    _check("vinf_groupnorm_clip_apply", st)
+    return y, mean, rstd
+
+
+def dda_clip_halo(F_total: int, f0: int, Fc: int, n_local: int = 16) -> tuple[int, int]:
+    """Frames before and after the clip [f0, f0+Fc) that its local windows reach."""
+    pre, post = ctypes.c_int(), ctypes.c_int()
+    st = load().vinf_dda_clip_halo(int(F_total), int(f0), int(Fc), int(n_local), ctypes.byref(pre),
+                                   ctypes.byref(post))
+    _check("vinf_dda_clip_halo", st)
+    return pre.value, post.value
+
+
+def dual_domain_attn_clip(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, F_total: int, f0: int, n_pre: int,
+                          n_post: int, k_global: torch.Tensor | None = None, v_global: torch.Tensor | None = None,
+                          out: torch.Tensor | None = None, head_dim: int = 64, n_local: int = 16,
+                          n_global: int = 16, scale: float = 0.0, stream=None) -> torch.Tensor:
+    """Attention of query frames f0 .. f0+Fc-1 (q: [Fc,H,W,C]) of an F_total-frame
+    video; k, v: [n_pre+Fc+n_post, H, W, C] (the clip with its context);
+    k_global, v_global: [n_global, H, W, C] frames floor(i*F_total/16) or None."""
+    _dev(q, "q")
+    Fc, H, W, C = _fhwc(q)
+    for name, t in (("k", k), ("v", v)):
+        _dev(t, name)
+        if tuple(t.shape) != (n_pre + Fc + n_post, H, W, C) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [{n_pre + Fc + n_post},{H},{W},{C}] of {q.dtype}")
+    for name, t in (("k_global", k_global), ("v_global", v_global)):
+        if t is not None:
+            _dev(t, name)
+            if tuple(t.shape) != (n_global, H, W, C) or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be [{n_global},{H},{W},{C}] of {q.dtype}")
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    st = load().vinf_dual_domain_attn_clip(_ptr(q), _ptr(k), _ptr(v), _ptr(k_global), _ptr(v_global), _ptr(o),
+                                            int(F_total), int(f0), Fc, int(n_pre), int(n_post), H, W, C, head_dim,
+                                            n_local, n_global, float(scale), _dtype_code(q),
+                                            _stream(q.device, stream))
+    _check("vinf_dual_domain_attn_clip", st)
     return o

@@ -59,6 +59,31 @@ static vinf_status check_f32(const char* fn, const char* name, const void* p) {
     return VINF_OK;
 }
 
+static vinf_status check_f64(const char* fn, const char* name, const void* p, bool required) {
+    if (!p) return required ? fail(VINF_ERR_INVALID_ARG, "%s: %s is NULL", fn, name) : VINF_OK;
+    if (!aligned(p, 8)) return fail(VINF_ERR_INVALID_ARG, "%s: %s is not 8-byte aligned", fn, name);
+    return VINF_OK;
+}
+
+// First frame of the local window of query frame t in an F-frame video
+// (n_local consecutive frames centred on t, shifted inward at the ends).
+static int64_t window_start(int64_t t, int64_t F, int64_t n_local) {
+    int64_t st = t - n_local / 2, hi = F - n_local > 0 ? F - n_local : 0;
+    return st < 0 ? 0 : (st > hi ? hi : st);
+}
+
+// Context frames a clip's local windows reach before and after it.
+static void clip_halo(int64_t F, int64_t f0, int64_t Fc, int64_t n_local, int64_t* pre, int64_t* post) {
+    if (n_local <= 0) {
+        *pre = *post = 0;
+        return;
+    }
+    const int64_t nl = n_local < F ? n_local : F;
+    const int64_t a = window_start(f0, F, n_local), b = window_start(f0 + Fc - 1, F, n_local) + nl;
+    *pre = f0 - a;
+    *post = b - (f0 + Fc) > 0 ? b - (f0 + Fc) : 0;
+}
+
 #define VINF_TRY(expr)                         \
     do {                                       \
         vinf_status s_ = (expr);               \
@@ -111,6 +136,67 @@ vinf_status vinf_groupnorm_global(const void* x, void* y, const float* gamma, co
                             (hipStream_t)stream);
 }
 
+// Shared checks of the two clip GroupNorm calls.
+static vinf_status check_gn_clip(const char* fn, const void* x, int F, int H, int W, int C, int groups, int F_total,
+                                 vinf_dtype dt, void* workspace, size_t workspace_bytes, size_t* bytes, size_t* need) {
+    VINF_TRY(check_shape(fn, F, H, W, C, dt, bytes));
+    VINF_TRY(check_tensor(fn, "x", x, true));
+    if (groups < 1 || C % groups) return fail(VINF_ERR_INVALID_ARG, "%s: C=%d not divisible by groups=%d", fn, C, groups);
+    if (F_total < F) return fail(VINF_ERR_INVALID_ARG, "%s: F_total=%d is smaller than the clip's F=%d", fn, F_total, F);
+    const int vec = dt == VINF_BF16 ? 8 : 4;
+    if (C / vec > 1024) return fail(VINF_ERR_UNSUPPORTED, "%s: C=%d exceeds %d", fn, C, 1024 * vec);
+    *need = groupnorm_workspace((int64_t)F * H * W, C, groups, dt);
+    if (!workspace || workspace_bytes < *need)
+        return fail(VINF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, *need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(VINF_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", fn);
+    if (overlap(workspace, *need, x, *bytes)) return fail(VINF_ERR_INVALID_ARG, "%s: workspace overlaps x", fn);
+    return VINF_OK;
+}
+
+vinf_status vinf_groupnorm_clip_sums(const void* x, const double* mean_sums, double* sums, int F, int H, int W, int C,
+                                     int groups, int F_total, vinf_dtype dt, void* workspace, size_t workspace_bytes,
+                                     vinf_stream stream) {
+    const char* fn = "vinf_groupnorm_clip_sums";
+    size_t bytes, need;
+    VINF_TRY(check_gn_clip(fn, x, F, H, W, C, groups, F_total, dt, workspace, workspace_bytes, &bytes, &need));
+    VINF_TRY(check_f64(fn, "mean_sums", mean_sums, false));
+    VINF_TRY(check_f64(fn, "sums", sums, true));
+    const size_t sb = (size_t)groups * sizeof(double);
+    if (overlap(sums, sb, x, bytes) || overlap(sums, sb, workspace, need) || overlap(sums, sb, mean_sums, sb))
+        return fail(VINF_ERR_INVALID_ARG, "%s: sums overlaps x, the workspace or mean_sums", fn);
+    const double n_total = (double)F_total * H * W * (C / groups);
+    return launch_groupnorm_clip_sums(x, mean_sums, sums, (int64_t)F * H * W, C, groups, n_total, dt, workspace,
+                                      (hipStream_t)stream);
+}
+
+vinf_status vinf_groupnorm_clip_apply(const void* x, void* y, const float* gamma, const float* beta, const double* sums,
+                                      const double* sq_sums, float* mean_out, float* rstd_out, int F, int H, int W,
+                                      int C, int groups, int F_total, float eps, vinf_dtype dt, void* workspace,
+                                      size_t workspace_bytes, vinf_stream stream) {
+    const char* fn = "vinf_groupnorm_clip_apply";
+    size_t bytes, need;
+    VINF_TRY(check_gn_clip(fn, x, F, H, W, C, groups, F_total, dt, workspace, workspace_bytes, &bytes, &need));
+    VINF_TRY(check_tensor(fn, "y", y, true));
+    VINF_TRY(check_f32(fn, "gamma", gamma));
+    VINF_TRY(check_f32(fn, "beta", beta));
+    VINF_TRY(check_f32(fn, "mean_out", mean_out));
+    VINF_TRY(check_f32(fn, "rstd_out", rstd_out));
+    VINF_TRY(check_f64(fn, "sums", sums, true));
+    VINF_TRY(check_f64(fn, "sq_sums", sq_sums, true));
+    if (!(eps >= 0.f)) return fail(VINF_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+    if (y != x && overlap(x, bytes, y, bytes))
+        return fail(VINF_ERR_INVALID_ARG, "%s: y partially overlaps x (only y == x is allowed)", fn);
+    const size_t st = (size_t)groups * sizeof(float);
+    if (overlap(workspace, need, y, bytes) || overlap(mean_out, st, x, bytes) || overlap(mean_out, st, y, bytes) ||
+        overlap(rstd_out, st, x, bytes) || overlap(rstd_out, st, y, bytes) || overlap(workspace, need, mean_out, st) ||
+        overlap(workspace, need, rstd_out, st))
+        return fail(VINF_ERR_INVALID_ARG, "%s: workspace / statistics overlap a tensor", fn);
+    const double n_total = (double)F_total * H * W * (C / groups);
+    return launch_groupnorm_clip_apply(x, y, gamma, beta, sums, sq_sums, mean_out, rstd_out, (int64_t)F * H * W, C,
+                                       groups, n_total, eps, dt, workspace, (hipStream_t)stream);
+}
+
 vinf_status vinf_temporal_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
                                 const float* bias, void* y, int F, int H, int W, int C, vinf_dtype dt,
                                 vinf_stream stream) {
@@ -133,6 +219,17 @@ vinf_status vinf_temporal_conv3(const void* x, const void* ctx_pre, const void* 
     return launch_conv3(x, ctx_pre, ctx_post, weight, bias, y, F, H * W, C, dt, (hipStream_t)stream);
 }
 
+// Shared checks of the attention calls: head layout and key-set sizes.
+static vinf_status check_dda_heads(const char* fn, int C, int head_dim, int n_local, int n_global, float scale) {
+    if (head_dim != 64) return fail(VINF_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64)", fn, head_dim);
+    if (C % head_dim) return fail(VINF_ERR_INVALID_ARG, "%s: C=%d not a multiple of head_dim", fn, C);
+    if ((n_local != 16 && n_local != 0) || (n_global != 16 && n_global != 0) || n_local + n_global == 0)
+        return fail(VINF_ERR_UNSUPPORTED, "%s: n_local=%d n_global=%d (each 16 or 0, not both 0)", fn, n_local,
+                    n_global);
+    if (!(scale == scale)) return fail(VINF_ERR_INVALID_ARG, "%s: scale is NaN", fn);
+    return VINF_OK;
+}
+
 vinf_status vinf_dual_domain_attn(const void* q, const void* k, const void* v, void* o, int F, int H, int W, int C,
                                   int head_dim, int n_local, int n_global, float scale, vinf_dtype dt,
                                   vinf_stream stream) {
@@ -143,15 +240,72 @@ vinf_status vinf_dual_domain_attn(const void* q, const void* k, const void* v, v
     VINF_TRY(check_tensor(fn, "k", k, true));
     VINF_TRY(check_tensor(fn, "v", v, true));
     VINF_TRY(check_tensor(fn, "o", o, true));
-    if (head_dim != 64) return fail(VINF_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64)", fn, head_dim);
-    if (C % head_dim) return fail(VINF_ERR_INVALID_ARG, "%s: C=%d not a multiple of head_dim", fn, C);
-    if (n_local != 16 || n_global != 16)
-        return fail(VINF_ERR_UNSUPPORTED, "%s: n_local=%d n_global=%d (only 16 and 16)", fn, n_local, n_global);
-    if (!(scale == scale)) return fail(VINF_ERR_INVALID_ARG, "%s: scale is NaN", fn);
+    VINF_TRY(check_dda_heads(fn, C, head_dim, n_local, n_global, scale));
     if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
         return fail(VINF_ERR_INVALID_ARG, "%s: o overlaps q, k or v", fn);
     if (scale <= 0.f) scale = 0.125f;  // 1/sqrt(64)
-    return launch_dda(q, k, v, o, F, H * W, C, scale, dt, (hipStream_t)stream);
+    return launch_dda(q, k, v, nullptr, nullptr, o, F, 0, F, 0, F, H * W, C, n_local, n_global, scale, dt,
+                      (hipStream_t)stream);
+}
+
+vinf_status vinf_dda_clip_halo(int F_total, int f0, int Fc, int n_local, int* n_pre, int* n_post) {
+    const char* fn = "vinf_dda_clip_halo";
+    if (!n_pre || !n_post) return fail(VINF_ERR_INVALID_ARG, "%s: NULL output", fn);
+    if (F_total < 1 || Fc < 1 || f0 < 0 || (int64_t)f0 + Fc > F_total)
+        return fail(VINF_ERR_INVALID_ARG, "%s: clip [%d, %d+%d) not inside a %d-frame video", fn, f0, f0, Fc, F_total);
+    if (n_local < 0) return fail(VINF_ERR_INVALID_ARG, "%s: n_local=%d", fn, n_local);
+    int64_t pre, post;
+    clip_halo(F_total, f0, Fc, n_local, &pre, &post);
+    *n_pre = (int)pre;
+    *n_post = (int)post;
+    return VINF_OK;
+}
+
+vinf_status vinf_dual_domain_attn_clip(const void* q, const void* k, const void* v, const void* k_global,
+                                       const void* v_global, void* o, int F_total, int f0, int Fc, int n_pre,
+                                       int n_post, int H, int W, int C, int head_dim, int n_local, int n_global,
+                                       float scale, vinf_dtype dt, vinf_stream stream) {
+    const char* fn = "vinf_dual_domain_attn_clip";
+    size_t bytes, ext_bytes;
+    VINF_TRY(check_shape(fn, Fc, H, W, C, dt, &bytes));
+    if (n_pre < 0 || n_post < 0 || (int64_t)n_pre + Fc + n_post > 2147483647)
+        return fail(VINF_ERR_INVALID_ARG, "%s: n_pre=%d n_post=%d", fn, n_pre, n_post);
+    VINF_TRY(check_shape(fn, n_pre + Fc + n_post, H, W, C, dt, &ext_bytes));
+    VINF_TRY(check_tensor(fn, "q", q, true));
+    VINF_TRY(check_tensor(fn, "k", k, true));
+    VINF_TRY(check_tensor(fn, "v", v, true));
+    VINF_TRY(check_tensor(fn, "o", o, true));
+    VINF_TRY(check_tensor(fn, "k_global", k_global, false));
+    VINF_TRY(check_tensor(fn, "v_global", v_global, false));
+    VINF_TRY(check_dda_heads(fn, C, head_dim, n_local, n_global, scale));
+    if (f0 < 0 || (int64_t)f0 + Fc > F_total)
+        return fail(VINF_ERR_INVALID_ARG, "%s: clip [%d, %d+%d) not inside a %d-frame video", fn, f0, f0, Fc, F_total);
+    const int64_t kf0 = (int64_t)f0 - n_pre, kend = (int64_t)f0 + Fc + n_post;
+    if (kf0 < 0 || kend > F_total)
+        return fail(VINF_ERR_INVALID_ARG, "%s: context frames [%lld, %lld) fall outside the video", fn, (long long)kf0,
+                    (long long)kend);
+    int64_t need_pre, need_post;
+    clip_halo(F_total, f0, Fc, n_local, &need_pre, &need_post);
+    if (n_pre < need_pre || n_post < need_post)
+        return fail(VINF_ERR_INVALID_ARG, "%s: the local windows need %lld frames before and %lld after, got %d and %d",
+                    fn, (long long)need_pre, (long long)need_post, n_pre, n_post);
+    if ((k_global == nullptr) != (v_global == nullptr))
+        return fail(VINF_ERR_INVALID_ARG, "%s: give both k_global and v_global or neither", fn);
+    if (n_global > 0 && !k_global) {
+        for (int i = 0; i < n_global; ++i) {
+            const int64_t f = (int64_t)i * F_total / n_global;
+            if (f < kf0 || f >= kend)
+                return fail(VINF_ERR_INVALID_ARG, "%s: global frame %lld is not in k/v and k_global is NULL", fn,
+                            (long long)f);
+        }
+    }
+    const size_t gbytes = k_global ? (size_t)(n_global > 0 ? n_global : 16) * H * W * C * dtype_bytes(dt) : 0;
+    if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, ext_bytes) || overlap(o, bytes, v, ext_bytes) ||
+        overlap(o, bytes, k_global, gbytes) || overlap(o, bytes, v_global, gbytes))
+        return fail(VINF_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+    if (scale <= 0.f) scale = 0.125f;  // 1/sqrt(64)
+    return launch_dda(q, k, v, k_global, v_global, o, F_total, f0, Fc, (int)kf0, (int)kend, H * W, C, n_local,
+                      n_global, scale, dt, (hipStream_t)stream);
 }
 
 const char* vinf_status_string(vinf_status s) {

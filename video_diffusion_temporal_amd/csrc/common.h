@@ -67,11 +67,24 @@ vinf_status launch_groupnorm(const void* x, void* y, const float* gamma, const f
                              float* rstd_out, int64_t rows, int C, int groups, float eps, vinf_dtype dt,
                              void* workspace, hipStream_t stream);
 size_t groupnorm_workspace(int64_t rows, int C, int groups, vinf_dtype dt);
+// One clip's fp64 group sums (first pass: mean_sums null; second pass: about
+// the means mean_sums[g] / n_total).
+vinf_status launch_groupnorm_clip_sums(const void* x, const double* mean_sums, double* sums, int64_t rows, int C,
+                                       int groups, double n_total, vinf_dtype dt, void* workspace,
+                                       hipStream_t stream);
+// Normalise one clip with the statistics of the aggregated sums.
+vinf_status launch_groupnorm_clip_apply(const void* x, void* y, const float* gamma, const float* beta,
+                                        const double* sums, const double* sq_sums, float* mean_out, float* rstd_out,
+                                        int64_t rows, int C, int groups, double n_total, float eps, vinf_dtype dt,
+                                        void* workspace, hipStream_t stream);
 
 vinf_status launch_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
                          const float* bias, void* y, int F, int S, int C, vinf_dtype dt, hipStream_t stream);
 
-vinf_status launch_dda(const void* q, const void* k, const void* v, void* o, int F, int S, int C, float scale,
-                       vinf_dtype dt, hipStream_t stream);
+// Attention of query frames f0 .. f0+nq-1 of an F-frame video; k/v hold
+// frames kf0 .. kend-1; kg/vg the global rows or null (read from k/v).
+vinf_status launch_dda(const void* q, const void* k, const void* v, const void* kg, const void* vg, void* o,
+                       int F, int f0, int nq, int kf0, int kend, int S, int C, int n_local, int n_global,
+                       float scale, vinf_dtype dt, hipStream_t stream);
 
 }  // namespace vinf_host

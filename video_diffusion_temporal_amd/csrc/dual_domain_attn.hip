@@ -68,30 +68,39 @@ __device__ __forceinline__ int dda_start(int t, int F) {
 __device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
+// Frames and buffers of one call.  The video has F frames; the queries are
+// frames f0 .. f0+nq-1 (q and o row 0 is frame f0); k and v hold frames
+// kf0 .. kend-1 (row 0 is frame kf0).  kg and vg hold the global rows (row i
+// is frame floor(i*F/16)) or are null when k and v hold those frames.  The
+// whole video on its own is f0 = kf0 = 0, nq = kend = F, kg = vg = null.
+struct DdaGeo {
+    const void* kg;
+    const void* vg;
+    int F, f0, nq, kf0, kend;
+    int S, C, nstrips, nitems;
+    float sl2e;
+};
+
 struct DdaItem {
     int strip, t0;
 };
 
-__device__ __forceinline__ DdaItem dda_item(int idx, int nstrips) {
-    return DdaItem{idx % nstrips, (idx / nstrips) * DDA_TQ};
+__device__ __forceinline__ DdaItem dda_item(const DdaGeo& g, int idx) {
+    return DdaItem{idx % g.nstrips, g.f0 + (idx / g.nstrips) * DDA_TQ};
 }
 
 // Stage one work item into `buf` (256 threads, lt = 0..255) and load the q row
-// of query t0 + lt into qv.
+// of query t0 + lt into qv.  NL / NG: local / global keys present (16 or 0).
+template <int NL, int NG>
 __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t* __restrict__ q,
-                                          const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int F,
-                                          int C, int64_t rs, int heads, DdaItem it, int lt, uint32_t (&qv)[32]) {
+                                          const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                          const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
+                                          uint32_t (&qv)[32]) {
     const int s = it.strip / heads, h = it.strip % heads;
-    const int64_t col = (int64_t)s * C + h * DDA_D;
-    const int tlast = min(it.t0 + DDA_TQ, F) - 1;
-    const int lo = dda_start(it.t0, F);
-    const int stl = dda_start(tlast, F);
-    const int nkr = stl + DDA_L - lo;             // K rows [lo, lo+nkr), <= 271
-    const int plo = lo & ~1;
-    const int np = (stl + DDA_L + 2 - plo) >> 1;  // V pairs cover [plo, plo+2np), <= 137
+    const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int t = it.t0 + lt;
-    if (t < F) {
-        const uint16_t* qrow = q + t * rs + col;
+    if (t < g.f0 + g.nq) {
+        const uint16_t* qrow = q + (int64_t)(t - g.f0) * rs + col;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             u32x4_t u = *reinterpret_cast<const u32x4_t*>(qrow + c * 8);
@@ -101,76 +110,99 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
             qv[4 * c + 3] = u[3];
         }
     }
-    // local K rows: this thread's chunk c = lt&7 of rows lt>>3 + 32*i
-    {
-        const int c = lt & 7, r0 = lt >> 3;
-        const uint16_t* src = k + col + (int64_t)(lo + r0) * rs + c * 8;
-        char* dst = buf + DDA_LDS_KL + r0 * DDA_KSTR + c * 16;
-        u32x4_t u[(DDA_KROWS + 31) / 32];
+    if constexpr (NL > 0) {
+        const int tlast = min(it.t0 + DDA_TQ, g.f0 + g.nq) - 1;
+        const int lo = dda_start(it.t0, g.F);
+        const int stl = dda_start(tlast, g.F);
+        const int nkr = stl + DDA_L - lo;             // K rows [lo, lo+nkr), <= 271
+        const int plo = lo & ~1;
+        const int np = (stl + DDA_L + 2 - plo) >> 1;  // V pairs cover [plo, plo+2np), <= 137
+        // Frames outside [kf0, kend) are not in k/v: their rows are zero-filled
+        // (only frames past the video's last frame, or the unused half of a
+        // pair row, which carry no weight, fall outside).
+        // local K rows: this thread's chunk c = lt&7 of rows lt>>3 + 32*i
+        {
+            const int c = lt & 7, r0 = lt >> 3;
+            const uint16_t* src = k + col + (int64_t)(lo + r0 - g.kf0) * rs + c * 8;
+            char* dst = buf + DDA_LDS_KL + r0 * DDA_KSTR + c * 16;
+            u32x4_t u[(DDA_KROWS + 31) / 32];
 #pragma unroll
-        for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i) {
-            const int r = r0 + 32 * i;
-            u[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (r < nkr && lo + r < F) u[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(32 * i) * rs);
+            for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i) {
+                const int r = r0 + 32 * i;
+                u[i] = u32x4_t{0u, 0u, 0u, 0u};
+                if (r < nkr && lo + r < g.kend) u[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(32 * i) * rs);
+            }
+#pragma unroll
+            for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i)
+                if (r0 + 32 * i < nkr) *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_KSTR) = u[i];
         }
+        // local V as frame pairs: this thread's 8-dim group oc = lt&7 of pairs lt>>3 + 32*i
+        {
+            const int oc = lt & 7, p0 = lt >> 3;
+            const uint16_t* src = v + col + (int64_t)(plo + 2 * p0 - g.kf0) * rs + oc * 8;
+            char* dst = buf + DDA_LDS_VP + p0 * DDA_VSTR + oc * 32;
+            u32x4_t a[(DDA_VPAIRS + 31) / 32], b[(DDA_VPAIRS + 31) / 32];
 #pragma unroll
-        for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i)
-            if (r0 + 32 * i < nkr) *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_KSTR) = u[i];
-    }
-    // local V as frame pairs: this thread's 8-dim group oc = lt&7 of pairs lt>>3 + 32*i
-    {
-        const int oc = lt & 7, p0 = lt >> 3;
-        const uint16_t* src = v + col + (int64_t)(plo + 2 * p0) * rs + oc * 8;
-        char* dst = buf + DDA_LDS_VP + p0 * DDA_VSTR + oc * 32;
-        u32x4_t a[(DDA_VPAIRS + 31) / 32], b[(DDA_VPAIRS + 31) / 32];
+            for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
+                const int p = p0 + 32 * i, fa = plo + 2 * p;
+                a[i] = u32x4_t{0u, 0u, 0u, 0u};
+                b[i] = u32x4_t{0u, 0u, 0u, 0u};
+                if (p < np && fa >= g.kf0 && fa < g.kend)
+                    a[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i) * rs);
+                if (p < np && fa + 1 < g.kend)
+                    b[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i + 1) * rs);
+            }
 #pragma unroll
-        for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
-            const int p = p0 + 32 * i, fa = plo + 2 * p;
-            a[i] = u32x4_t{0u, 0u, 0u, 0u};
-            b[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (p < np && fa < F) a[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i) * rs);
-            if (p < np && fa + 1 < F) b[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i + 1) * rs);
-        }
-#pragma unroll
-        for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
-            if (p0 + 32 * i < np) {
-                u32x4_t w0 = {perm_lo(a[i][0], b[i][0]), perm_hi(a[i][0], b[i][0]), perm_lo(a[i][1], b[i][1]),
-                              perm_hi(a[i][1], b[i][1])};
-                u32x4_t w1 = {perm_lo(a[i][2], b[i][2]), perm_hi(a[i][2], b[i][2]), perm_lo(a[i][3], b[i][3]),
-                              perm_hi(a[i][3], b[i][3])};
-                *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR) = w0;
-                *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR + 16) = w1;
+            for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
+                if (p0 + 32 * i < np) {
+                    u32x4_t w0 = {perm_lo(a[i][0], b[i][0]), perm_hi(a[i][0], b[i][0]), perm_lo(a[i][1], b[i][1]),
+                                  perm_hi(a[i][1], b[i][1])};
+                    u32x4_t w1 = {perm_lo(a[i][2], b[i][2]), perm_hi(a[i][2], b[i][2]), perm_lo(a[i][3], b[i][3]),
+                                  perm_hi(a[i][3], b[i][3])};
+                    *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR) = w0;
+                    *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR + 16) = w1;
+                }
             }
         }
     }
-    // global K rows (threads 0..127) and V pairs (threads 128..191)
-    if (lt < DDA_G * 8) {
-        const int i = lt >> 3, c = lt & 7;
-        const int f = (int)(((int64_t)i * F) / DDA_G);
-        *reinterpret_cast<u32x4_t*>(buf + DDA_LDS_KG + i * 128 + c * 16) =
-            *reinterpret_cast<const u32x4_t*>(k + col + f * rs + c * 8);
-    } else if (lt < DDA_G * 8 + (DDA_G / 2) * 8) {
-        const int j = lt - DDA_G * 8;
-        const int p = j >> 3, oc = j & 7;
-        const int fa = (int)(((int64_t)(2 * p) * F) / DDA_G), fb = (int)(((int64_t)(2 * p + 1) * F) / DDA_G);
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(v + col + fa * rs + oc * 8);
-        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(v + col + fb * rs + oc * 8);
-        u32x4_t w0 = {perm_lo(a[0], b[0]), perm_hi(a[0], b[0]), perm_lo(a[1], b[1]), perm_hi(a[1], b[1])};
-        u32x4_t w1 = {perm_lo(a[2], b[2]), perm_hi(a[2], b[2]), perm_lo(a[3], b[3]), perm_hi(a[3], b[3])};
-        char* dst = buf + DDA_LDS_VG + p * 256 + oc * 32;
-        *reinterpret_cast<u32x4_t*>(dst) = w0;
-        *reinterpret_cast<u32x4_t*>(dst + 16) = w1;
+    if constexpr (NG > 0) {
+        // global K rows (threads 0..127) and V pairs (threads 128..191)
+        const uint16_t* kgb = g.kg ? static_cast<const uint16_t*>(g.kg) : k;
+        const uint16_t* vgb = g.vg ? static_cast<const uint16_t*>(g.vg) : v;
+        auto grow = [&](int i) -> int64_t {  // row of global frame i in kgb / vgb
+            return g.kg ? (int64_t)i : (int64_t)(((int64_t)i * g.F) / DDA_G) - g.kf0;
+        };
+        if (lt < DDA_G * 8) {
+            const int i = lt >> 3, c = lt & 7;
+            *reinterpret_cast<u32x4_t*>(buf + DDA_LDS_KG + i * 128 + c * 16) =
+                *reinterpret_cast<const u32x4_t*>(kgb + col + grow(i) * rs + c * 8);
+        } else if (lt < DDA_G * 8 + (DDA_G / 2) * 8) {
+            const int j = lt - DDA_G * 8;
+            const int p = j >> 3, oc = j & 7;
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p) * rs + oc * 8);
+            const u32x4_t b = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p + 1) * rs + oc * 8);
+            u32x4_t w0 = {perm_lo(a[0], b[0]), perm_hi(a[0], b[0]), perm_lo(a[1], b[1]), perm_hi(a[1], b[1])};
+            u32x4_t w1 = {perm_lo(a[2], b[2]), perm_hi(a[2], b[2]), perm_lo(a[3], b[3]), perm_hi(a[3], b[3])};
+            char* dst = buf + DDA_LDS_VG + p * 256 + oc * 32;
+            *reinterpret_cast<u32x4_t*>(dst) = w0;
+            *reinterpret_cast<u32x4_t*>(dst + 16) = w1;
+        }
     }
 }
 
 // Compute query t0 + lt of a staged work item from `buf`.
-__device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16_t* __restrict__ o, int F, int C,
-                                            int64_t rs, int heads, DdaItem it, int lt, const uint32_t (&qv)[32],
-                                            float sl2e) {
+template <int NL, int NG>
+__device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16_t* __restrict__ o,
+                                            const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
+                                            const uint32_t (&qv)[32]) {
+    constexpr int NK = NL + NG;                 // keys
+    constexpr int NLP = NL > 0 ? 9 : 0;         // local V pair rows
+    constexpr int NP = NLP + (NG > 0 ? 8 : 0);  // V pair rows
     const int t = it.t0 + lt;
-    if (t >= F) return;
+    if (t >= g.f0 + g.nq) return;
     const int s = it.strip / heads, h = it.strip % heads;
-    const int64_t col = (int64_t)s * C + h * DDA_D;
+    const int64_t col = (int64_t)s * g.C + h * DDA_D;
+    const int F = g.F;
     const int lo = dda_start(it.t0, F);
     const int plo = lo & ~1;
     const int nl = F < DDA_L ? F : DDA_L;
@@ -178,17 +210,17 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 
     // ---- scores: one K row (8 x 16 B) per key; the next row's reads are
     // issued before the current row's dot products ----
-    float sc[DDA_L + DDA_G];
+    float sc[NK];
     const char* krow = buf + DDA_LDS_KL + (st - lo) * DDA_KSTR;
     auto key_row = [&](int i) -> const char* {
-        return i < DDA_L ? krow + i * DDA_KSTR : buf + DDA_LDS_KG + (i - DDA_L) * 128;
+        return i < NL ? krow + i * DDA_KSTR : buf + DDA_LDS_KG + (i - NL) * 128;
     };
     u32x4_t kb[2][8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) kb[0][c] = *reinterpret_cast<const u32x4_t*>(key_row(0) + c * 16);
 #pragma unroll
-    for (int i = 0; i < DDA_L + DDA_G; ++i) {
-        if (i + 1 < DDA_L + DDA_G) {
+    for (int i = 0; i < NK; ++i) {
+        if (i + 1 < NK) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) kb[(i + 1) & 1][c] = *reinterpret_cast<const u32x4_t*>(key_row(i + 1) + c * 16);
         }
@@ -207,41 +239,43 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // ---- lane-local softmax (base 2, scale folded in) ----
     float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < DDA_L + DDA_G; ++j) {
-        sc[j] = (j < DDA_L && j >= nl) ? -INFINITY : sc[j] * sl2e;
+    for (int j = 0; j < NK; ++j) {
+        sc[j] = (j < NL && j >= nl) ? -INFINITY : sc[j] * g.sl2e;
         m = fmaxf(m, sc[j]);
     }
 #pragma unroll
-    for (int j = 0; j < DDA_L + DDA_G; ++j) sc[j] = __builtin_amdgcn_exp2f(sc[j] - m);
+    for (int j = 0; j < NK; ++j) sc[j] = __builtin_amdgcn_exp2f(sc[j] - m);
 
-    // weights as bf16 pairs matching the V pair rows
-    const int par = st & 1;
-    uint32_t wl[9], wg[8];
+    // weights as bf16 pairs matching the V pair rows: NLP local, then 8 global
+    uint32_t w[NP];
+    if constexpr (NL > 0) {
+        const int par = st & 1;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
-        float a_even = j < 8 ? sc[2 * j] : 0.f;          // par == 0: frames (st+2j, st+2j+1)
-        float b_even = j < 8 ? sc[2 * j + 1] : 0.f;
-        float a_odd = j > 0 ? sc[2 * j - 1] : 0.f;       // par == 1: frames (st+2j-1, st+2j)
-        float b_odd = j < 8 ? sc[2 * j] : 0.f;
-        wl[j] = par ? pack_bf16x2(a_odd, b_odd) : pack_bf16x2(a_even, b_even);
+        for (int j = 0; j < 9; ++j) {
+            float a_even = j < 8 ? sc[2 * j] : 0.f;          // par == 0: frames (st+2j, st+2j+1)
+            float b_even = j < 8 ? sc[2 * j + 1] : 0.f;
+            float a_odd = j > 0 ? sc[2 * j - 1] : 0.f;       // par == 1: frames (st+2j-1, st+2j)
+            float b_odd = j < 8 ? sc[2 * j] : 0.f;
+            w[j] = par ? pack_bf16x2(a_odd, b_odd) : pack_bf16x2(a_even, b_even);
+        }
     }
+    if constexpr (NG > 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wg[i] = pack_bf16x2(sc[DDA_L + 2 * i], sc[DDA_L + 2 * i + 1]);
+        for (int i = 0; i < 8; ++i) w[NLP + i] = pack_bf16x2(sc[NL + 2 * i], sc[NL + 2 * i + 1]);
+    }
     const uint32_t ones = 0x3f803f80u;  // (1.0, 1.0) in bf16
     float den = 0.f;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) den = dot2_bf16(wl[j], ones, den);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) den = dot2_bf16(wg[i], ones, den);
+    for (int j = 0; j < NP; ++j) den = dot2_bf16(w[j], ones, den);
 
-    // ---- weighted sum of V: 9 local + 8 global pair rows, next row's
-    // reads issued before the current row's dot products ----
+    // ---- weighted sum of V over the NP pair rows, next row's reads issued
+    // before the current row's dot products ----
     float acc[DDA_D];
 #pragma unroll
     for (int d = 0; d < DDA_D; ++d) acc[d] = 0.f;
     const char* vrow = buf + DDA_LDS_VP + ((st - plo) >> 1) * DDA_VSTR;
     auto val_row = [&](int j) -> const char* {
-        return j < 9 ? vrow + j * DDA_VSTR : buf + DDA_LDS_VG + (j - 9) * 256;
+        return j < NLP ? vrow + j * DDA_VSTR : buf + DDA_LDS_VG + (j - NLP) * 256;
     };
     // half rows (32 dims, 8 x 16 B) double-buffered: step 2j + hh reads
     // dims 32*hh.. of pair row j
@@ -249,15 +283,15 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 #pragma unroll
     for (int c = 0; c < 8; ++c) vb[0][c] = *reinterpret_cast<const u32x4_t*>(val_row(0) + c * 16);
 #pragma unroll
-    for (int step = 0; step < 34; ++step) {
+    for (int step = 0; step < 2 * NP; ++step) {
         const int j = step >> 1, hh = step & 1;
-        if (step + 1 < 34) {
+        if (step + 1 < 2 * NP) {
             const int jn = (step + 1) >> 1, hn = (step + 1) & 1;
 #pragma unroll
             for (int c = 0; c < 8; ++c)
                 vb[(step + 1) & 1][c] = *reinterpret_cast<const u32x4_t*>(val_row(jn) + hn * 128 + c * 16);
         }
-        const uint32_t wj = j < 9 ? wl[j] : wg[j - 9];
+        const uint32_t wj = w[j];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
 #pragma unroll
@@ -267,13 +301,13 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     }
 
     const float inv = 1.f / den;
-    uint16_t* orow = o + t * rs + col;
+    uint16_t* orow = o + (int64_t)(t - g.f0) * rs + col;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        u32x4_t w;
+        u32x4_t wv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[8 * c + 2 * e] * inv, acc[8 * c + 2 * e + 1] * inv);
-        *reinterpret_cast<u32x4_t*>(orow + c * 8) = w;
+        for (int e = 0; e < 4; ++e) wv[e] = pack_bf16x2(acc[8 * c + 2 * e] * inv, acc[8 * c + 2 * e + 1] * inv);
+        *reinterpret_cast<u32x4_t*>(orow + c * 8) = wv;
     }
 }
 
@@ -283,17 +317,18 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 // Phase p: half 0 stages its item p/2 (p even) or computes item (p-1)/2 (p
 // odd); half 1 stages item (p-1)/2 (p odd) or computes item (p-2)/2 (p even,
 // p >= 2).  Every thread runs every phase and barrier.
+template <int NL, int NG>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-         uint16_t* __restrict__ o, int F, int S, int C, int nstrips, int nitems, float sl2e) {
+         uint16_t* __restrict__ o, DdaGeo g) {
     __shared__ __attribute__((aligned(16))) char lds[2 * DDA_LDS_BYTES];
-    const int heads = C / DDA_D;
-    const int64_t rs = (int64_t)S * C;
+    const int heads = g.C / DDA_D;
+    const int64_t rs = (int64_t)g.S * g.C;
     const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), lt = threadIdx.x & 255;
     char* buf = lds + half * DDA_LDS_BYTES;
     const int G = gridDim.x, w = blockIdx.x;
-    const int mine = w < nitems ? (nitems - w + G - 1) / G : 0;     // items of this workgroup
-    const int jh = (mine - half + 1) / 2;                            // items of this half
+    const int mine = w < g.nitems ? (g.nitems - w + G - 1) / G : 0;  // items of this workgroup
+    const int jh = (mine - half + 1) / 2;                             // items of this half
     const int j0 = (mine + 1) / 2, j1 = mine / 2;
     const int phases = max(2 * j0, 2 * j1 + 1);
     uint32_t qv[32];
@@ -302,11 +337,11 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         if (rel >= 0) {
             const int j = rel >> 1;
             if (j < jh) {
-                const DdaItem it = dda_item(w + (2 * j + half) * G, nstrips);
+                const DdaItem it = dda_item(g, w + (2 * j + half) * G);
                 if ((rel & 1) == 0)
-                    dda_stage(buf, q, k, v, F, C, rs, heads, it, lt, qv);
+                    dda_stage<NL, NG>(buf, q, k, v, g, rs, heads, it, lt, qv);
                 else
-                    dda_compute(buf, o, F, C, rs, heads, it, lt, qv, sl2e);
+                    dda_compute<NL, NG>(buf, o, g, rs, heads, it, lt, qv);
             }
         }
         __syncthreads();
@@ -314,31 +349,37 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
 }
 
 // float32 I/O: one query per thread, keys read through the cache.
+// n_local, n_global: 16 or 0.
 __global__ void __launch_bounds__(64) dda_f32(const float* __restrict__ q, const float* __restrict__ k,
-                                              const float* __restrict__ v, float* __restrict__ o, int F, int S,
-                                              int C, float sl2e) {
-    const int heads = C / DDA_D;
-    const int64_t qi = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (t, s, h) flattened
-    if (qi >= (int64_t)F * S * heads) return;
+                                              const float* __restrict__ v, float* __restrict__ o, DdaGeo g,
+                                              int n_local, int n_global) {
+    const int heads = g.C / DDA_D;
+    const int64_t qi = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (t - f0, s, h) flattened
+    if (qi >= (int64_t)g.nq * g.S * heads) return;
     const int h = (int)(qi % heads);
-    const int s = (int)((qi / heads) % S);
-    const int t = (int)(qi / ((int64_t)heads * S));
-    const int64_t rs = (int64_t)S * C, col = (int64_t)s * C + h * DDA_D;
-    const int nl = F < DDA_L ? F : DDA_L;
+    const int s = (int)((qi / heads) % g.S);
+    const int i = (int)(qi / ((int64_t)heads * g.S));
+    const int t = g.f0 + i, F = g.F;
+    const int64_t rs = (int64_t)g.S * g.C, col = (int64_t)s * g.C + h * DDA_D;
+    const int nl = F < n_local ? F : n_local;
     const int st = dda_start(t, F);
-    int keys[DDA_L + DDA_G];
+    const float* kgb = g.kg ? static_cast<const float*>(g.kg) : k;
+    const float* vgb = g.vg ? static_cast<const float*>(g.vg) : v;
+    // row offset (elements) of key j in k / v (local) or kgb / vgb (global)
+    auto row = [&](int j) -> int64_t {
+        const int gi = j - nl;
+        return j < nl ? (int64_t)(st + j - g.kf0) * rs
+                      : (g.kg ? (int64_t)gi * rs : (((int64_t)gi * F) / DDA_G - g.kf0) * rs);
+    };
     float sc[DDA_L + DDA_G];
-    const int n = nl + DDA_G;
-    for (int j = 0; j < DDA_L + DDA_G; ++j) {
-        keys[j] = j < nl ? st + j : (j < n ? (int)(((int64_t)(j - nl) * F) / DDA_G) : 0);
-    }
-    const float* qr = q + t * rs + col;
+    const int n = nl + n_global;
+    const float* qr = q + (int64_t)i * rs + col;
     float m = -INFINITY;
     for (int j = 0; j < n; ++j) {
-        const float* kr = k + keys[j] * rs + col;
+        const float* kr = (j < nl ? k : kgb) + row(j) + col;
         float a = 0.f;
         for (int d = 0; d < DDA_D; ++d) a = fmaf(qr[d], kr[d], a);
-        sc[j] = a * sl2e;
+        sc[j] = a * g.sl2e;
         m = fmaxf(m, sc[j]);
     }
     float acc[DDA_D];
@@ -347,11 +388,11 @@ __global__ void __launch_bounds__(64) dda_f32(const float* __restrict__ q, const
     for (int j = 0; j < n; ++j) {
         float p = __builtin_amdgcn_exp2f(sc[j] - m);
         den += p;
-        const float* vr = v + keys[j] * rs + col;
+        const float* vr = (j < nl ? v : vgb) + row(j) + col;
         for (int d = 0; d < DDA_D; ++d) acc[d] = fmaf(p, vr[d], acc[d]);
     }
     float inv = 1.f / den;
-    float* orow = o + t * rs + col;
+    float* orow = o + (int64_t)i * rs + col;
     for (int d = 0; d < DDA_D; ++d) orow[d] = acc[d] * inv;
 }
 
@@ -360,30 +401,49 @@ __global__ void __launch_bounds__(64) dda_f32(const float* __restrict__ q, const
 namespace vinf_host {
 using namespace vinf;
 
-vinf_status launch_dda(const void* q, const void* k, const void* v, void* o, int F, int S, int C, float scale,
-                       vinf_dtype dt, hipStream_t st) {
-    const float sl2e = scale * 1.4426950408889634f;
+vinf_status launch_dda(const void* q, const void* k, const void* v, const void* kg, const void* vg, void* o,
+                       int F, int f0, int nq, int kf0, int kend, int S, int C, int n_local, int n_global,
+                       float scale, vinf_dtype dt, hipStream_t st) {
     const int heads = C / DDA_D;
+    DdaGeo g;
+    g.kg = kg;
+    g.vg = vg;
+    g.F = F;
+    g.f0 = f0;
+    g.nq = nq;
+    g.kf0 = kf0;
+    g.kend = kend;
+    g.S = S;
+    g.C = C;
+    g.nstrips = S * heads;
+    g.nitems = 0;
+    g.sl2e = scale * 1.4426950408889634f;
     if (dt == VINF_BF16) {
-        const int nstrips = S * heads;
-        const int nfb = (F + DDA_TQ - 1) / DDA_TQ;
-        const int64_t items = (int64_t)nstrips * nfb;
+        const int nfb = (nq + DDA_TQ - 1) / DDA_TQ;
+        const int64_t items = (int64_t)g.nstrips * nfb;
         if (items > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "dual_domain_attn: too many work items");
+        g.nitems = (int)items;
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             return fail(VINF_ERR_HIP, "dual_domain_attn: cannot query the device");
         // one persistent workgroup per CU, each with at least two items
-        const int64_t grid = std::min<int64_t>(cus, (items + 1) / 2);
-        hipLaunchKernelGGL(dda_bf16, dim3((uint32_t)grid), dim3(512), 0, st, static_cast<const uint16_t*>(q),
-                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
-                           F, S, C, nstrips, (int)items, sl2e);
+        const dim3 grid((uint32_t)std::min<int64_t>(cus, (items + 1) / 2)), block(512);
+        const uint16_t *qb = static_cast<const uint16_t*>(q), *kb = static_cast<const uint16_t*>(k),
+                       *vb = static_cast<const uint16_t*>(v);
+        uint16_t* ob = static_cast<uint16_t*>(o);
+        if (n_local > 0 && n_global > 0)
+            hipLaunchKernelGGL((dda_bf16<DDA_L, DDA_G>), grid, block, 0, st, qb, kb, vb, ob, g);
+        else if (n_local > 0)
+            hipLaunchKernelGGL((dda_bf16<DDA_L, 0>), grid, block, 0, st, qb, kb, vb, ob, g);
+        else
+            hipLaunchKernelGGL((dda_bf16<0, DDA_G>), grid, block, 0, st, qb, kb, vb, ob, g);
     } else {
-        const int64_t nq = (int64_t)F * S * heads;
-        const int64_t blocks = (nq + 63) / 64;
+        const int64_t nqs = (int64_t)nq * S * heads;
+        const int64_t blocks = (nqs + 63) / 64;
         if (blocks > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "dual_domain_attn: grid too large");
         hipLaunchKernelGGL(dda_f32, dim3((uint32_t)blocks), dim3(64), 0, st, static_cast<const float*>(q),
-                           static_cast<const float*>(k), static_cast<const float*>(v), static_cast<float*>(o), F, S,
-                           C, sl2e);
+                           static_cast<const float*>(k), static_cast<const float*>(v), static_cast<float*>(o), g,
+                           n_local, n_global);
     }
     return check_launch("dual_domain_attn");
 }

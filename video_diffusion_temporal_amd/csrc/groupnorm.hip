@@ -22,6 +22,14 @@
 //                       b_c = beta_c - mean_g*a_c, forward again (its first
 //                       rows are the ones the second sweep read last).
 // HBM traffic: three reads and one write of the tensor.
+//
+// Clip form (the clip-parallelism paragraph: every device holds one clip and
+// the statistics are aggregated across devices): the same sweeps over one
+// clip write the fp64 group sums instead of a statistic (gn_finalize with
+// dsum); the caller adds the clips' sums (one all-reduce per pass) and
+// gn_stats_from_sums turns the totals into mean_g / rstd_g for the second
+// sweep and the apply.  The statistic expressions are shared, so one clip
+// covering the whole video reproduces the whole-video path bit for bit.
 #include <math.h>
 
 #include "common.h"
@@ -125,12 +133,20 @@ __global__ void __launch_bounds__(1024) gn_partial(const void* __restrict__ x, c
     }
 }
 
+// The statistics from fp64 group sums over n voxel-channels.
+__device__ __forceinline__ float gn_mean_of(double sum, double n) { return (float)(sum / n); }
+__device__ __forceinline__ float gn_rstd_of(double sq_sum, double n, float eps) {
+    return (float)(1.0 / sqrt(sq_sum / n + (double)eps));
+}
+
 // One block per group: fixed-order fp64 sum of the group's partials.
-// stats = [mean_0..mean_{G-1}, rstd_0..rstd_{G-1}] (float).
+// stats = [mean_0..mean_{G-1}, rstd_0..rstd_{G-1}] (float).  With stats
+// non-null the block writes its statistic there (and to out, if non-null);
+// with dsum non-null it writes the raw fp64 sum to dsum[g].
 template <bool SECOND>
 __global__ void __launch_bounds__(256) gn_finalize(const float* __restrict__ partial, float* __restrict__ stats,
-                                                   float* __restrict__ out, int B, int C, int cpg, int G,
-                                                   double inv_n, float eps) {
+                                                   float* __restrict__ out, double* __restrict__ dsum, int B, int C,
+                                                   int cpg, int G, double n, float eps) {
     __shared__ double red[256];
     const int g = blockIdx.x;
     const int64_t items = (int64_t)B * cpg;
@@ -160,10 +176,29 @@ __global__ void __launch_bounds__(256) gn_finalize(const float* __restrict__ par
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        double m = red[0] * inv_n;
-        float v = SECOND ? (float)(1.0 / sqrt(m + (double)eps)) : (float)m;
-        stats[(SECOND ? G : 0) + g] = v;
-        if (out) out[g] = v;
+        if (dsum) dsum[g] = red[0];
+        if (stats) {
+            const float v = SECOND ? gn_rstd_of(red[0], n, eps) : gn_mean_of(red[0], n);
+            stats[(SECOND ? G : 0) + g] = v;
+            if (out) out[g] = v;
+        }
+    }
+}
+
+// stats[g] = mean_g from sum[g]; with sq_sum non-null also stats[G+g] = rstd_g.
+__global__ void __launch_bounds__(256) gn_stats_from_sums(const double* __restrict__ sum,
+                                                          const double* __restrict__ sq_sum, float* __restrict__ stats,
+                                                          float* __restrict__ mean_out, float* __restrict__ rstd_out,
+                                                          int G, double n, float eps) {
+    for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < G; g += gridDim.x * blockDim.x) {
+        const float m = gn_mean_of(sum[g], n);
+        stats[g] = m;
+        if (mean_out) mean_out[g] = m;
+        if (sq_sum) {
+            const float r = gn_rstd_of(sq_sum[g], n, eps);
+            stats[G + g] = r;
+            if (rstd_out) rstd_out[g] = r;
+        }
     }
 }
 
@@ -226,26 +261,78 @@ size_t groupnorm_workspace(int64_t rows, int C, int groups, vinf_dtype dt) {
     return align256((size_t)g.blocks * C * sizeof(float)) + align256(2 * (size_t)groups * sizeof(float));
 }
 
+struct GnBufs {
+    GnGeom g;
+    float* partial;  // [B][C]
+    float* stats;    // [2G]: mean_g, rstd_g
+};
+
+static GnBufs gn_bufs(int64_t rows, int C, vinf_dtype dt, void* ws) {
+    GnBufs b;
+    b.g = gn_geom(rows, C, dt);
+    b.partial = static_cast<float*>(ws);
+    b.stats = reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)b.g.blocks * C * sizeof(float)));
+    return b;
+}
+
+template <bool BF16, bool SECOND>
+static void sweep(const void* x, const GnBufs& b, int64_t rows, int C, int cpg, hipStream_t st) {
+    const size_t lds = (size_t)b.g.RB * C * sizeof(float);
+    hipLaunchKernelGGL((gn_partial<BF16, SECOND>), dim3(b.g.blocks), dim3(b.g.threads), lds, st, x, b.stats,
+                       b.partial, rows, C, b.g.V, b.g.RB, cpg);
+}
+
+template <bool BF16>
+static void apply(const void* x, void* y, const float* gamma, const float* beta, const GnBufs& b, int64_t rows, int C,
+                  int cpg, int G, hipStream_t st) {
+    hipLaunchKernelGGL((gn_apply<BF16>), dim3(b.g.blocks), dim3(b.g.threads), 0, st, x, y, b.stats, gamma, beta,
+                       rows, C, b.g.V, b.g.RB, cpg, G);
+}
+
 template <bool BF16>
 static vinf_status run(const void* x, void* y, const float* gamma, const float* beta, float* mean_out,
                        float* rstd_out, int64_t rows, int C, int G, float eps, void* ws, hipStream_t st) {
-    GnGeom g = gn_geom(rows, C, BF16 ? VINF_BF16 : VINF_F32);
-    float* partial = static_cast<float*>(ws);
-    float* stats = reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)g.blocks * C * sizeof(float)));
+    const GnBufs b = gn_bufs(rows, C, BF16 ? VINF_BF16 : VINF_F32, ws);
     const int cpg = C / G;
-    const double inv_n = 1.0 / ((double)rows * (double)cpg);
-    const size_t lds = (size_t)g.RB * C * sizeof(float);
-    hipLaunchKernelGGL((gn_partial<BF16, false>), dim3(g.blocks), dim3(g.threads), lds, st, x, stats, partial, rows,
-                       C, g.V, g.RB, cpg);
-    hipLaunchKernelGGL((gn_finalize<false>), dim3(G), dim3(256), 0, st, partial, stats, mean_out, g.blocks, C, cpg,
-                       G, inv_n, eps);
-    hipLaunchKernelGGL((gn_partial<BF16, true>), dim3(g.blocks), dim3(g.threads), lds, st, x, stats, partial, rows,
-                       C, g.V, g.RB, cpg);
-    hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(256), 0, st, partial, stats, rstd_out, g.blocks, C, cpg,
-                       G, inv_n, eps);
-    hipLaunchKernelGGL((gn_apply<BF16>), dim3(g.blocks), dim3(g.threads), 0, st, x, y, stats, gamma, beta, rows, C,
-                       g.V, g.RB, cpg, G);
+    const double n = (double)rows * (double)cpg;
+    sweep<BF16, false>(x, b, rows, C, cpg, st);
+    hipLaunchKernelGGL((gn_finalize<false>), dim3(G), dim3(256), 0, st, b.partial, b.stats, mean_out, nullptr,
+                       b.g.blocks, C, cpg, G, n, eps);
+    sweep<BF16, true>(x, b, rows, C, cpg, st);
+    hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(256), 0, st, b.partial, b.stats, rstd_out, nullptr,
+                       b.g.blocks, C, cpg, G, n, eps);
+    apply<BF16>(x, y, gamma, beta, b, rows, C, cpg, G, st);
     return check_launch("groupnorm");
+}
+
+template <bool BF16>
+static vinf_status run_clip_sums(const void* x, const double* mean_sums, double* sums, int64_t rows, int C, int G,
+                                 double n_total, void* ws, hipStream_t st) {
+    const GnBufs b = gn_bufs(rows, C, BF16 ? VINF_BF16 : VINF_F32, ws);
+    const int cpg = C / G;
+    if (mean_sums) {
+        hipLaunchKernelGGL(gn_stats_from_sums, dim3((G + 255) / 256), dim3(256), 0, st, mean_sums, nullptr, b.stats,
+                           nullptr, nullptr, G, n_total, 0.f);
+        sweep<BF16, true>(x, b, rows, C, cpg, st);
+        hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(256), 0, st, b.partial, nullptr, nullptr, sums,
+                           b.g.blocks, C, cpg, G, n_total, 0.f);
+    } else {
+        sweep<BF16, false>(x, b, rows, C, cpg, st);
+        hipLaunchKernelGGL((gn_finalize<false>), dim3(G), dim3(256), 0, st, b.partial, nullptr, nullptr, sums,
+                           b.g.blocks, C, cpg, G, n_total, 0.f);
+    }
+    return check_launch("groupnorm_clip_sums");
+}
+
+template <bool BF16>
+static vinf_status run_clip_apply(const void* x, void* y, const float* gamma, const float* beta, const double* sums,
+                                  const double* sq_sums, float* mean_out, float* rstd_out, int64_t rows, int C, int G,
+                                  double n_total, float eps, void* ws, hipStream_t st) {
+    const GnBufs b = gn_bufs(rows, C, BF16 ? VINF_BF16 : VINF_F32, ws);
+    hipLaunchKernelGGL(gn_stats_from_sums, dim3((G + 255) / 256), dim3(256), 0, st, sums, sq_sums, b.stats, mean_out,
+                       rstd_out, G, n_total, eps);
+    apply<BF16>(x, y, gamma, beta, b, rows, C, C / G, G, st);
+    return check_launch("groupnorm_clip_apply");
 }
 
 vinf_status launch_groupnorm(const void* x, void* y, const float* gamma, const float* beta, float* mean_out,
@@ -254,6 +341,25 @@ vinf_status launch_groupnorm(const void* x, void* y, const float* gamma, const f
     if (dt == VINF_BF16)
         return run<true>(x, y, gamma, beta, mean_out, rstd_out, rows, C, groups, eps, workspace, stream);
     return run<false>(x, y, gamma, beta, mean_out, rstd_out, rows, C, groups, eps, workspace, stream);
+}
+
+vinf_status launch_groupnorm_clip_sums(const void* x, const double* mean_sums, double* sums, int64_t rows, int C,
+                                       int groups, double n_total, vinf_dtype dt, void* workspace,
+                                       hipStream_t stream) {
+    if (dt == VINF_BF16)
+        return run_clip_sums<true>(x, mean_sums, sums, rows, C, groups, n_total, workspace, stream);
+    return run_clip_sums<false>(x, mean_sums, sums, rows, C, groups, n_total, workspace, stream);
+}
+
+vinf_status launch_groupnorm_clip_apply(const void* x, void* y, const float* gamma, const float* beta,
+                                        const double* sums, const double* sq_sums, float* mean_out, float* rstd_out,
+                                        int64_t rows, int C, int groups, double n_total, float eps, vinf_dtype dt,
+                                        void* workspace, hipStream_t stream) {
+    if (dt == VINF_BF16)
+        return run_clip_apply<true>(x, y, gamma, beta, sums, sq_sums, mean_out, rstd_out, rows, C, groups, n_total,
+                                    eps, workspace, stream);
+    return run_clip_apply<false>(x, y, gamma, beta, sums, sq_sums, mean_out, rstd_out, rows, C, groups, n_total, eps,
+                                 workspace, stream);
 }
 
 }  // namespace vinf_host
