@@ -3,8 +3,9 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
 leg may import this package.  It wraps ``oracle.c`` (plain fp64 C, see
 ``oracle.h`` for the passages each routine follows) with ctypes over numpy
-arrays.  Inputs are float32 arrays (dt = F32) or uint16 bf16 bit patterns
-(dt = BF16) shaped [F, H, W, C] (or [F, S, C]); outputs are float64 arrays
+arrays.  Inputs are float32 arrays (dt = F32), uint16 bf16 bit patterns
+(dt = BF16) or float64 arrays (dt = F64, e.g. an unrounded intermediate)
+shaped [F, H, W, C] (or [F, S, C]); outputs are float64 arrays
 [F, n_locs, C] for the requested spatial locations (flattened h*W + w).
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 _i64p = ctypes.POINTER(ctypes.c_int64)
 
 
@@ -62,7 +63,9 @@ def _dt(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle inputs are float32 or uint16 bf16 bits, got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs are float32, uint16 bf16 bits or float64, got {a.dtype}")
 
 
 def _c(a):

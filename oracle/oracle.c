@@ -17,6 +17,7 @@
 /* ---- helpers ---------------------------------------------------------- */
 
 static double load(const void* p, int dt, int64_t i) {
+    if (dt == 2) return ((const double*)p)[i];
     if (dt == 0) return (double)((const float*)p)[i];
     uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
     float f;
@@ -25,6 +26,7 @@ static double load(const void* p, int dt, int64_t i) {
 }
 
 double oracle_round_to(double v, int dt) {
+    if (dt == 2) return v;
     if (dt == 0) return (double)(float)v;
     /* bf16 keeps 8 significant bits: v = m * 2^e with 0.5 <= |m| < 1, so the
      * nearest bf16 is nearbyint(m * 2^8) * 2^(e-8) (ties to even under the
@@ -111,7 +113,7 @@ static void gn_pass(void* vctx, int64_t r0, int64_t r1, int tid) {
 
 int oracle_gn_stats(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, double eps,
                     double* mean, double* var, double* rstd, int nthreads) {
-    if (!x || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || G < 1 || C % G) return 1;
+    if (!x || dt < 0 || dt > 2 || F < 1 || S < 1 || C < 1 || G < 1 || C % G) return 1;
     nthreads = resolve_threads(nthreads);
     int64_t rows = F * S, cg = C / G;
     double n_g = (double)rows * (double)cg;
@@ -149,7 +151,7 @@ int oracle_gn_stats(const void* x, int dt, int64_t F, int64_t S, int64_t C, int6
  * (mean == NULL) or of (x - mean[g])^2. */
 int oracle_gn_clip_sums(const void* x, int dt, int64_t F, int64_t S, int64_t C, int64_t G, const double* mean,
                         double* sums, int nthreads) {
-    if (!x || !sums || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || G < 1 || C % G) return 1;
+    if (!x || !sums || dt < 0 || dt > 2 || F < 1 || S < 1 || C < 1 || G < 1 || C % G) return 1;
     nthreads = resolve_threads(nthreads);
     double* partial = (double*)calloc((size_t)nthreads * (size_t)G, sizeof(double));
     if (!partial) return 2;
@@ -251,7 +253,7 @@ static void conv_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
 int oracle_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* w,
                  const double* bias, int dt, int64_t F, int64_t S, int64_t C, const int64_t* locs,
                  int64_t n_locs, double* y, int nthreads) {
-    if (!x || !w || !y || !locs || (dt != 0 && dt != 1) || F < 1 || S < 1 || C < 1 || n_locs < 0) return 1;
+    if (!x || !w || !y || !locs || dt < 0 || dt > 2 || F < 1 || S < 1 || C < 1 || n_locs < 0) return 1;
     for (int64_t i = 0; i < n_locs; ++i)
         if (locs[i] < 0 || locs[i] >= S) return 1;
     nthreads = resolve_threads(nthreads);
@@ -352,7 +354,7 @@ static void dda_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
 }
 
 static int dda_run(dda_ctx* c, int nthreads) {
-    if (!c->q || !c->k || !c->v || !c->o || !c->locs || (c->dt != 0 && c->dt != 1) || c->F < 1 || c->S < 1 ||
+    if (!c->q || !c->k || !c->v || !c->o || !c->locs || c->dt < 0 || c->dt > 2 || c->F < 1 || c->S < 1 ||
         c->C < 1 || c->dh < 1 || c->C % c->dh || c->L < 0 || c->Gk < 0 || c->L + c->Gk < 1 || c->n_locs < 0 ||
         (!c->kg) != (!c->vg))
         return 1;
@@ -407,7 +409,7 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
                  double eps, int head_dim, int n_local, int n_global, double scale,
                  const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
                  double* gn_exact, double* conv_exact, double* mean, double* rstd, int nthreads) {
-    if (!out || !w || n_locs < 1) return 1;
+    if (!out || !w || n_locs < 1 || (dt != 0 && dt != 1)) return 1; /* intermediates are rounded to dt */
     size_t n = (size_t)(F * n_locs * C);
     double* a = (double*)malloc(sizeof(double) * n);
     double* b = (double*)malloc(sizeof(double) * n);

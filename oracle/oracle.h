@@ -23,8 +23,9 @@
  * Readings of points the page leaves open are stated at each function.
  *
  * Tensors are dense channels-last [F][S][C] (S = H*W spatial locations), given
- * as float32 (dt = 0) or bf16 bit patterns (dt = 1); inputs are widened
- * exactly to double.  Outputs are double, for a list of spatial locations
+ * as float32 (dt = 0), bf16 bit patterns (dt = 1) or float64 (dt = 2: an
+ * unrounded intermediate, such as the exact GroupNorm output); inputs are
+ * widened exactly to double.  oracle_chain takes dt 0 or 1 only.  Outputs are double, for a list of spatial locations
  * `locs` (n_locs entries), laid out [F][n_locs][C].  Temporal modules act on
  * each spatial location independently, so a location subset is exact.
  *

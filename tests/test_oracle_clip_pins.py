@@ -186,3 +186,35 @@ def test_gn_clip_sums_aggregate_to_whole_video_stats():
     # a clip's own mean is not the global one (frames 0..4 sit below it)
     m0 = oracle.gn_clip_sums(x[0:5], G) / (5 * S * C // G)
     assert np.all(m0 < mean)
+
+
+# ------------------------------------------------ float64 (exact) inputs
+
+def test_float64_inputs_match_the_narrow_types():
+    # A float64 array holding the same values as a float32 or bf16 one gives
+    # identical results: the type only changes how values are read.
+    F, S, C, G = 19, 3, 64, 8
+    for dt in (synth.F32, synth.BF16):
+        x = randn((F, S, C), 220 + dt, dt)
+        x64 = widen(x).astype(np.float64)
+        w = randn((3, C, C), 222 + dt, dt, 0.1)
+        w64 = widen(w).astype(np.float64)
+        assert np.array_equal(oracle.conv3(x64, w64), oracle.conv3(x, w))
+        assert np.array_equal(oracle.dda(x64, x64, x64), oracle.dda(x, x, x))
+        for a, b in zip(oracle.gn_stats(x64, G), oracle.gn_stats(x, G)):
+            assert np.array_equal(a, b)
+
+
+def test_conv_of_exact_groupnorm_brute_force():
+    # The reference of a conv that consumes an unrounded GroupNorm output:
+    # the oracle's conv over float64 input against a numpy sum of three
+    # shifted matrix products.
+    F, S, C, G = 11, 4, 32, 4
+    x = randn((F, S, C), 230, synth.BF16)
+    gn, _, _ = oracle.groupnorm(x, G)                 # float64 [F, S, C]
+    w = randn((3, C, C), 231, synth.BF16, 0.2)
+    wf = widen(w).astype(np.float64)
+    pad = np.zeros((F + 2, S, C))
+    pad[1:-1] = gn
+    ref = sum(pad[k:k + F] @ wf[k].T for k in range(3))
+    assert np.abs(oracle.conv3(gn, wf) - ref).max() < 1e-12
