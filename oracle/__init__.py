@@ -48,7 +48,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_gn_clip_sums.argtypes = [vp, i, i64, i64, i64, i64, vp, vp, i]
         L.oracle_dda_clip.argtypes = [vp, vp, vp, vp, vp, i, i64, i64, i64, i64, i64, i64, i64, i, i, i, d, vp, i64,
                                       vp, i]
-        L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, vp, i64, vp, vp, vp, vp, vp, vp, vp, i]
+        L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, i, vp, i64, vp, vp, vp, vp, vp, vp,
+                                   vp, i]
         L.oracle_round_to.argtypes = [d, i]
         L.oracle_round_to.restype = d
         for fn in ("oracle_gn_stats", "oracle_groupnorm", "oracle_conv3", "oracle_dda_keys", "oracle_dda",
@@ -190,12 +191,14 @@ def dda_clip(q, k, v, F_total, f0, kf0, k_glob=None, v_glob=None, head_dim=64, n
 
 
 def chain(x, w, G, eps=1e-5, head_dim=64, n_local=16, n_global=16, scale=0.0, locs=None, nthreads=0,
-          intermediates=False, exact=False):
+          intermediates=False, exact=False, round_gn=True):
     """GroupNorm -> conv3 -> dual-domain attention (Q = K = V), at sampled locations.
 
     Returns (out, mean, rstd); with intermediates=True (out, gn, conv, mean,
     rstd) where gn and conv are the rounded intermediates; with exact=True
     also (gn_exact, conv_exact), the intermediates before rounding.
+    round_gn=False: GroupNorm folded into the conv, so the conv reads the
+    exact GroupNorm output (gn is then that exact output).
     """
     x, w = _c(x), _c(w)
     F, S, C = _fsc(x)
@@ -208,7 +211,7 @@ def chain(x, w, G, eps=1e-5, head_dim=64, n_local=16, n_global=16, scale=0.0, lo
     cx = np.empty_like(out) if exact else None
     mean, rstd = np.empty(G), np.empty(G)
     rc = lib().oracle_chain(_ptr(x), _ptr(w), _dt(x), F, S, C, G, eps, head_dim, n_local, n_global, scale,
-                            _ptr(locs), locs.size, _ptr(out), _ptr(gn), _ptr(cv), _ptr(gx), _ptr(cx), _ptr(mean),
+                            1 if round_gn else 0, _ptr(locs), locs.size, _ptr(out), _ptr(gn), _ptr(cv), _ptr(gx), _ptr(cx), _ptr(mean),
                             _ptr(rstd), nthreads)
     if rc:
         raise ValueError(f"oracle_chain rc={rc}")

@@ -401,12 +401,15 @@ int oracle_dda_clip(const void* q, const void* k, const void* v, const void* k_g
 
 /* ---- The three modules in a row --------------------------------------- */
 /* Each module's output is a tensor of the I/O type, so intermediates are
- * rounded to dt before they feed the next module.  The location subset stays
- * exact: conv and attention never mix spatial locations, and the GroupNorm
- * statistics are taken over the whole tensor. */
+ * rounded to dt before they feed the next module.  With round_gn == 0 the
+ * GroupNorm output is not a tensor of its own (GroupNorm folded into the
+ * conv): the conv then reads the exact GroupNorm values and only the conv
+ * output is rounded.  The location subset stays exact: conv and attention
+ * never mix spatial locations, and the GroupNorm statistics are taken over
+ * the whole tensor. */
 
 int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int64_t C, int64_t G,
-                 double eps, int head_dim, int n_local, int n_global, double scale,
+                 double eps, int head_dim, int n_local, int n_global, double scale, int round_gn,
                  const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
                  double* gn_exact, double* conv_exact, double* mean, double* rstd, int nthreads) {
     if (!out || !w || n_locs < 1 || (dt != 0 && dt != 1)) return 1; /* intermediates are rounded to dt */
@@ -415,17 +418,25 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
     double* b = (double*)malloc(sizeof(double) * n);
     void* ta = malloc((dt == 0 ? 4 : 2) * n);
     int64_t* seq = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_locs);
-    if (!a || !b || !ta || !seq) {
+    double* w64 = round_gn ? NULL : (double*)malloc(sizeof(double) * (size_t)(3 * C * C));
+    if (!a || !b || !ta || !seq || (!round_gn && !w64)) {
         free(a);
         free(b);
         free(ta);
         free(seq);
+        free(w64);
         return 2;
     }
     int rc = oracle_groupnorm(x, dt, F, S, C, G, eps, NULL, NULL, locs, n_locs, a, mean, rstd, nthreads);
     /* The sampled columns become a dense [F][n_locs][C] tensor in dt. */
     for (int64_t i = 0; i < n_locs; ++i) seq[i] = i;
-    if (rc == 0) {
+    if (rc == 0 && !round_gn) {
+        /* the conv reads the exact GroupNorm values, and the weights widened alike */
+        if (gn_exact) memcpy(gn_exact, a, sizeof(double) * n);
+        if (gn_out) memcpy(gn_out, a, sizeof(double) * n);
+        for (int64_t i = 0; i < 3 * C * C; ++i) w64[i] = load(w, dt, i);
+        rc = oracle_conv3(a, NULL, NULL, w64, NULL, 2, F, n_locs, C, seq, n_locs, b, nthreads);
+    } else if (rc == 0) {
         if (gn_exact) memcpy(gn_exact, a, sizeof(double) * n);
         for (size_t i = 0; i < n; ++i) {
             a[i] = oracle_round_to(a[i], dt);
@@ -462,5 +473,6 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
     free(b);
     free(ta);
     free(seq);
+    free(w64);
     return rc;
 }

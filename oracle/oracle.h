@@ -94,10 +94,12 @@ int oracle_dda_clip(const void* q, const void* k, const void* v, const void* k_g
 
 /* GroupNorm (identity affine) -> round to dt -> conv3 (zero padded, no bias)
  * -> round to dt -> dual-domain attention with Q = K = V = the conv output.
- * gn_out / conv_out ([F][n_locs][C], rounded values) and gn_exact /
- * conv_exact (the same before rounding) may be NULL. */
+ * round_gn == 0 skips the first rounding: the conv reads the exact GroupNorm
+ * output (GroupNorm folded into the conv, no GroupNorm tensor in between).
+ * gn_out / conv_out ([F][n_locs][C], the values the next module reads) and
+ * gn_exact / conv_exact (the same before rounding) may be NULL. */
 int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int64_t C, int64_t G,
-                 double eps, int head_dim, int n_local, int n_global, double scale,
+                 double eps, int head_dim, int n_local, int n_global, double scale, int round_gn,
                  const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
                  double* gn_exact, double* conv_exact, double* mean, double* rstd, int nthreads);
 

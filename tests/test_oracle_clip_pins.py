@@ -218,3 +218,23 @@ def test_conv_of_exact_groupnorm_brute_force():
     pad[1:-1] = gn
     ref = sum(pad[k:k + F] @ wf[k].T for k in range(3))
     assert np.abs(oracle.conv3(gn, wf) - ref).max() < 1e-12
+
+
+def test_chain_without_groupnorm_rounding_composes_the_modules():
+    # The fused reading: the conv reads the exact GroupNorm output, only the
+    # conv output is rounded before the attention.
+    import math
+    F, S, C, G = 20, 6, 128, 8
+    x = randn((F, S, C), 240, synth.BF16)
+    w = randn((3, C, C), 241, synth.BF16, 1 / math.sqrt(3 * C))
+    out, gn, cv, mean, rstd = oracle.chain(x, w, G, intermediates=True, round_gn=False)
+    y, m2, r2 = oracle.groupnorm(x, G)
+    assert np.array_equal(gn, y) and np.array_equal(mean, m2) and np.array_equal(rstd, r2)
+    cx = oracle.conv3(y, widen(w).astype(np.float64))
+    cv_ref = np.vectorize(lambda a: oracle.round_to(a, synth.BF16))(cx)
+    assert np.array_equal(cv, cv_ref)
+    cb = (cv.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(out, oracle.dda(cb, cb, cb))
+    # the rounded reading differs from it only through the GroupNorm rounding
+    out_r, gn_r, _, _, _ = oracle.chain(x, w, G, intermediates=True)
+    assert not np.array_equal(gn_r, gn) and np.abs(gn_r - gn).max() <= 2.0 ** -8 * np.abs(gn).max()
