@@ -6,7 +6,10 @@ A step is one pass of the whole temporal module over one synthetic latent:
 GroupNorm with whole-video statistics -> kernel-3 temporal conv (zero pads at
 the video ends) -> dual-domain attention with Q = K = V = the conv output, at
 F=1024 frames, 64x40 locations, C=320 (5 heads of 64), bf16, 32 groups -- the
-VideoCrafter2 latent shape at 512x320.  Inputs and every intermediate live in
+VideoCrafter2 latent shape at 512x320.  The GroupNorm normalisation is applied
+inside the conv (statistics call + fused conv call, bit for bit the same
+result), so the normalised tensor is never written; the chain that writes it
+is timed too ("chain_unfused").  Inputs and every intermediate live in
 HBM before the timed region starts; no allocation happens inside it.
 
 Prints ONE JSON line: voxels/s (F*H*W per step), per-module times, the
@@ -50,6 +53,8 @@ def algorithmic_work(F, H, W, C, b=2):
         "conv3_bf16": dict(bound="mfma", bytes=vox * 2 * C * b + 3 * C * C * b, flops=vox * 6 * C * C),
         # two statistic sweeps + apply: 3 reads and 1 write
         "groupnorm": dict(bound="hbm", bytes=vox * 4 * C * b, flops=vox * 8 * C),
+        # the two statistic sweeps alone: 2 reads
+        "groupnorm_stats": dict(bound="hbm", bytes=vox * 2 * C * b, flops=vox * 4 * C),
     }
 
 
@@ -110,7 +115,7 @@ def hbm_entry(ms, nbytes):
     return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
 
 
-def next_rows(vinf, x, cv, gn, G, stream, steps, work):
+def next_rows(vinf, x, cv, G, stream, steps):
     """The clip-parallel forms and the attention ablations, each timed alone.
 
     Clip form: one of eight clips of a 2300-frame video (frames 864..1151,
@@ -128,7 +133,7 @@ def next_rows(vinf, x, cv, gn, G, stream, steps, work):
     pre, post = vinf.dda_clip_halo(F_total, f0, Fc)
     n_ext = pre + Fc + post
     q = cv[:Fc]
-    k = gn[:n_ext]
+    k = x[:n_ext]
     v = torch.empty((n_ext, H, W, C), device=x.device, dtype=x.dtype)
     v.copy_(cv[F - n_ext:].flip(0))
     kg = torch.empty((16, H, W, C), device=x.device, dtype=x.dtype)
@@ -182,6 +187,8 @@ def main():
                     help="skip the attention call on three distinct Q, K, V tensors")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the clip-form and ablation measurements")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip timing the chain with the normalised tensor written out")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} requested)",
@@ -207,53 +214,70 @@ def main():
     mean = torch.empty(G, device=dev)
     rstd = torch.empty(G, device=dev)
     ws = torch.empty(vinf.groupnorm_workspace_bytes(F, H, W, C, G, x.dtype), device=dev, dtype=torch.uint8)
+    cws = torch.empty(vinf.temporal_conv3_gn_workspace_bytes(C, x.dtype), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
     if args.copy_calibration:
         g.copy_(x)  # 2 * F*H*W*C bytes of plain HBM traffic, before anything else
         torch.cuda.synchronize()
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        vinf.groupnorm_global(x, G, out=g, mean_out=mean, rstd_out=rstd, workspace=ws, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        vinf.temporal_conv3(g, wt, out=cv, stream=stream)
-        if ev:
-            ev[2].record(stream)
-        vinf.dual_domain_attn(cv, cv, cv, out=o, stream=stream)
-        if ev:
-            ev[3].record(stream)
+    # The step: GroupNorm statistics -> the conv of the GroupNorm output, the
+    # normalisation applied to the conv's input tiles -> attention with Q = K = V.
+    fused = [
+        ("groupnorm_stats", lambda: vinf.groupnorm_stats(x, G, mean_out=mean, rstd_out=rstd, workspace=ws,
+                                                         stream=stream)),
+        ("conv3_bf16", lambda: vinf.temporal_conv3_gn(x, wt, mean, rstd, out=cv, workspace=cws, stream=stream)),
+        ("dda_bf16", lambda: vinf.dual_domain_attn(cv, cv, cv, out=o, stream=stream)),
+    ]
+    # The same chain with the normalised tensor written and read back.
+    unfused = [
+        ("groupnorm", lambda: vinf.groupnorm_global(x, G, out=g, mean_out=mean, rstd_out=rstd, workspace=ws,
+                                                    stream=stream)),
+        ("conv3_bf16", lambda: vinf.temporal_conv3(g, wt, out=cv, stream=stream)),
+        ("dda_bf16", lambda: vinf.dual_domain_attn(cv, cv, cv, out=o, stream=stream)),
+    ]
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    mod_ms = {"groupnorm": 0.0, "conv3_bf16": 0.0, "dda_bf16": 0.0}
-    for e in evs:
-        mod_ms["groupnorm"] += e[0].elapsed_time(e[1])
-        mod_ms["conv3_bf16"] += e[1].elapsed_time(e[2])
-        mod_ms["dda_bf16"] += e[2].elapsed_time(e[3])
-    mod_ms = {k: v / args.steps for k, v in mod_ms.items()}
-    ms_step = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
-    vox = F * H * W
+    def run_chain(mods):
+        """Warm up, then time args.steps steps with HIP events on the launch stream around every module."""
+        for _ in range(args.warmup):
+            for _, f in mods:
+                f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(mods) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            for j, (_, f) in enumerate(mods):
+                evs[i][j].record(stream)
+                f()
+            evs[i][-1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        mod_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, (name, _) in enumerate(mods)}
+        return evs[0][0].elapsed_time(evs[-1][-1]) / args.steps, mod_ms, wall
 
     work = algorithmic_work(F, H, W, C)
-    kernels = {}
-    for k, ms in mod_ms.items():
-        wk = work[k]
-        gbs = wk["bytes"] / (ms * 1e-3) / 1e9
-        tfl = wk["flops"] / (ms * 1e-3) / 1e12
-        kernels[k] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfl, 2),
+
+    def kernel_table(mod_ms):
+        out = {}
+        for k, ms in mod_ms.items():
+            wk = work[k]
+            gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+            tfl = wk["flops"] / (ms * 1e-3) / 1e12
+            out[k] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(tfl, 2),
                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                       "frac_mfma_bf16": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4) if k == "conv3_bf16" else None}
-    # dominant single-launch kernel (the GroupNorm module is five launches)
+        return out
+
+    unfused_chain = None
+    if not args.no_unfused:
+        ms_u, mod_u, _ = run_chain(unfused)
+        unfused_chain = {"ms_per_step": round(ms_u, 4), "voxels_per_s": F * H * W / (ms_u * 1e-3),
+                         "kernels": kernel_table(mod_u),
+                         "chain": "groupnorm (stats + apply, normalised tensor written) -> conv3 -> dual_domain_attn"}
+    ms_step, mod_ms, wall = run_chain(fused)
+    vox = F * H * W
+    kernels = kernel_table(mod_ms)
+    # dominant single-kernel module (the GroupNorm statistics are four launches)
     dom = max(("conv3_bf16", "dda_bf16"), key=lambda k: mod_ms[k])
     wk = work[dom]
     if wk["bound"] == "hbm":
@@ -273,7 +297,7 @@ def main():
         kd = torch.empty_like(x)
         vd = torch.empty_like(x)
         kd.copy_(cv.flip(0))      # frames reversed: different data, same distribution
-        vd.copy_(g)
+        vd.copy_(x)
         for _ in range(2):
             vinf.dual_domain_attn(cv, kd, vd, out=o, stream=stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -287,10 +311,11 @@ def main():
         gbs = work["dda_bf16"]["bytes"] / (ms * 1e-3) / 1e9
         distinct = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         del kd, vd
-        step()  # restore o to the chain's output for the parity check
-        torch.cuda.synchronize()
 
-    nxt = None if args.no_next else next_rows(vinf, x, cv, g, G, stream, args.steps, work)
+    nxt = None if args.no_next else next_rows(vinf, x, cv, G, stream, args.steps)
+    for _, f in fused:  # o = the step's output again, for the parity check
+        f()
+    torch.cuda.synchronize()
 
     parity = None
     if not args.no_check:
@@ -319,10 +344,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) latent, conv weights N(0,1/(3C)))",
         "config": {"workload": WORKLOAD["name"], "F": F, "H": H, "W": W, "C": C, "heads": C // 64, "groups": G,
-                   "n_local": 16, "n_global": 16, "chain": "groupnorm->conv3->dual_domain_attn"},
+                   "n_local": 16, "n_global": 16,
+                   "chain": "groupnorm statistics -> conv3 of the groupnorm output (normalisation applied to the "
+                            "conv's input tiles in LDS) -> dual_domain_attn"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "chain_unfused": unfused_chain,
         "dda_bf16_distinct_qkv": distinct,
         "next_rows": nxt,
         "wall_s_timed": wall,

@@ -106,6 +106,48 @@ vinf_status vinf_temporal_conv3(const void* x, const void* ctx_pre, const void* 
                                 int C, vinf_dtype dt, vinf_stream stream);
 
 /*
+ * GroupNorm statistics only: the two sweeps of vinf_groupnorm_global
+ * (mean first, then the deviation about it), writing mean_g and
+ * 1/sqrt(var_g + eps) without normalising the tensor.  Arguments, limits and
+ * workspace as vinf_groupnorm_global; mean_out and rstd_out are required.
+ * The values are bit for bit those vinf_groupnorm_global reports.
+ */
+vinf_status vinf_groupnorm_stats(const void* x, float* mean_out, float* rstd_out, int F, int H, int W, int C,
+                                 int groups, float eps, vinf_dtype dt, void* workspace, size_t workspace_bytes,
+                                 vinf_stream stream);
+
+/*
+ * The temporal conv of the GroupNorm output, with GroupNorm applied inside
+ * the conv (the temporal-modules paragraph puts GroupNorm and Conv in a row;
+ * the normalised tensor is never written to memory):
+ *
+ *   y = conv3(g),  g[f,h,w,c] = x[f,h,w,c] * a_c + b_c,
+ *   a_c = rstd_g * gamma_c,  b_c = beta_c - mean_g * a_c   (fp32, rounded to dt)
+ *
+ * with conv3 as vinf_temporal_conv3.  g is formed and rounded exactly as
+ * vinf_groupnorm_global's apply writes it, so the result is bit for bit that
+ * of the apply followed by vinf_temporal_conv3.  ctx_pre / ctx_post are raw
+ * neighbouring frames, normalised the same way; absent, the pads are zeros of
+ * g, as in vinf_temporal_conv3.
+ *
+ * x, y      [F][H][W][C] in dt (y must not overlap any input).
+ * weight    [3][C][C] in dt; bias [C] float32 or NULL.
+ * mean, rstd  [groups] float32 (vinf_groupnorm_stats, or
+ *           vinf_groupnorm_clip_apply without x for a clip).
+ * gamma, beta [C] float32 or NULL (1 and 0).
+ * workspace device scratch of vinf_temporal_conv3_gn_workspace_bytes(C, dt)
+ *           bytes (the per-channel a_c, b_c), 256-byte aligned, not
+ *           overlapping any argument.
+ * Limits    as vinf_temporal_conv3; C % groups == 0.
+ */
+size_t vinf_temporal_conv3_gn_workspace_bytes(int C, vinf_dtype dt);
+vinf_status vinf_temporal_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_post,
+                                   const void* weight, const float* bias, const float* mean,
+                                   const float* rstd, const float* gamma, const float* beta, int groups,
+                                   void* y, int F, int H, int W, int C, vinf_dtype dt, void* workspace,
+                                   size_t workspace_bytes, vinf_stream stream);
+
+/*
  * Dual-domain temporal attention (dual-domain attention paragraph, and the
  * paragraph that sets both context sizes to 16): at each spatial location and
  * head, query frame t attends over the concatenation of a local context and a
@@ -158,6 +200,8 @@ vinf_status vinf_dual_domain_attn(const void* q, const void* k, const void* v, v
  * gamma, beta, mean_out, rstd_out, eps, workspace: as vinf_groupnorm_global,
  *           with the workspace sized by vinf_groupnorm_workspace_bytes for
  *           this clip's F.
+ * vinf_groupnorm_clip_apply with x and y both NULL writes only mean_out and
+ *           rstd_out (both required then), e.g. for vinf_temporal_conv3_gn.
  * The sums and statistics use the same kernels and expressions as
  * vinf_groupnorm_global, so a single clip with F_total == F gives the same
  * bits as that call.

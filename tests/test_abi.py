@@ -234,3 +234,60 @@ def gn_clip_apply(**kw):
 ])
 def test_groupnorm_clip_apply_rejects(kw, status):
     assert gn_clip_apply(**kw) == status
+
+
+# ------------------------------------------------- GroupNorm folded into the conv
+
+def gn_stats(**kw):
+    L = vinf.load()
+    a = dict(x=A, mean=B, rstd=B + 256, F=16, H=8, W=5, C=64, G=8, eps=1e-5, dt=F32, ws=Cp, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = L.vinf_groupnorm_workspace_bytes(16, 8, 5, 64, 8, F32)
+    return L.vinf_groupnorm_stats(a["x"], a["mean"], a["rstd"], a["F"], a["H"], a["W"], a["C"], a["G"], a["eps"],
+                                  a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(mean=None), INVALID), (dict(rstd=None), INVALID), (dict(mean=B + 2), INVALID),
+    (dict(G=7), INVALID), (dict(eps=-1.0), INVALID), (dict(F=0), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=16), WORKSPACE),
+    (dict(mean=A + 64), INVALID), (dict(rstd=B + 16), INVALID),   # inside x / overlapping mean
+])
+def test_groupnorm_stats_rejects(kw, status):
+    assert gn_stats(**kw) == status
+
+
+def test_conv3_gn_workspace_bytes():
+    L = vinf.load()
+    n = L.vinf_temporal_conv3_gn_workspace_bytes(320, BF16)
+    assert n >= 2 * 320 * 4 and n % 256 == 0   # the per-channel a and b tables
+    assert L.vinf_temporal_conv3_gn_workspace_bytes(320, F32) == n
+    assert L.vinf_temporal_conv3_gn_workspace_bytes(0, BF16) == 0
+    assert L.vinf_temporal_conv3_gn_workspace_bytes(64, 9) == 0
+
+
+def conv_gn(**kw):
+    L = vinf.load()
+    a = dict(x=A, pre=None, post=None, w=B, bias=None, mean=D, rstd=D + 256, gamma=None, beta=None, G=8, y=Cp,
+             F=16, H=8, W=5, C=64, dt=BF16, ws=E, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = L.vinf_temporal_conv3_gn_workspace_bytes(64, BF16)
+    return L.vinf_temporal_conv3_gn(a["x"], a["pre"], a["post"], a["w"], a["bias"], a["mean"], a["rstd"],
+                                    a["gamma"], a["beta"], a["G"], a["y"], a["F"], a["H"], a["W"], a["C"], a["dt"],
+                                    a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID), (dict(mean=None), INVALID),
+    (dict(rstd=None), INVALID), (dict(rstd=D + 2), INVALID), (dict(gamma=Fp + 1), INVALID),
+    (dict(G=7), INVALID), (dict(G=0), INVALID), (dict(F=0), INVALID),
+    (dict(C=48, G=8), UNSUPPORTED),                 # bf16 MFMA tiles need C % 32
+    (dict(ws=None), WORKSPACE), (dict(wsb=8), WORKSPACE), (dict(ws=E + 16), WORKSPACE),
+    (dict(y=A), INVALID), (dict(y=B + 64), INVALID),   # y overlaps x / the weights
+    (dict(ws=B), INVALID), (dict(ws=Cp + 256), INVALID),   # workspace overlaps the weights / y
+    (dict(mean=Cp + 64), INVALID),                 # statistics inside y
+])
+def test_conv3_gn_rejects(kw, status):
+    assert conv_gn(**kw) == status

@@ -8,6 +8,11 @@ Call names match the C ABI in include/vinf.h:
     temporal_conv3(x, weight, ctx_pre=None, ...)     -> y
     dual_domain_attn(q, k, v, ...)                   -> o
 
+GroupNorm applied inside the conv (the normalised tensor is never written):
+
+    groupnorm_stats(x, groups, eps=1e-5)                      -> (mean, rstd)
+    temporal_conv3_gn(x, weight, mean, rstd, ...)             -> y = conv3(GroupNorm(x))
+
 and the clip-parallel forms (one clip of a longer video plus its context):
 
     groupnorm_clip_sums(x, groups, F_total, mean_sums=None)  -> sums (float64 [groups])
@@ -27,7 +32,8 @@ import os
 import torch
 
 __all__ = ["groupnorm_global", "groupnorm_workspace_bytes", "temporal_conv3", "dual_domain_attn",
-           "groupnorm_clip_sums", "groupnorm_clip_apply", "dda_clip_halo", "dual_domain_attn_clip", "VinfError",
+           "groupnorm_clip_sums", "groupnorm_clip_apply", "dda_clip_halo", "dual_domain_attn_clip", "groupnorm_stats",
+           "temporal_conv3_gn", "temporal_conv3_gn_workspace_bytes", "VinfError",
            "library_path", "load", "VINF_F32", "VINF_BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -62,8 +68,13 @@ def load() -> ctypes.CDLL:
         L.vinf_groupnorm_clip_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
         L.vinf_dda_clip_halo.argtypes = [i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
         L.vinf_dual_domain_attn_clip.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, f, i, vp]
+        L.vinf_groupnorm_stats.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        L.vinf_temporal_conv3_gn_workspace_bytes.argtypes = [i, i]
+        L.vinf_temporal_conv3_gn_workspace_bytes.restype = sz
+        L.vinf_temporal_conv3_gn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, vp, sz, vp]
         for fn in ("vinf_groupnorm_global", "vinf_temporal_conv3", "vinf_dual_domain_attn", "vinf_groupnorm_clip_sums",
-                   "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo", "vinf_dual_domain_attn_clip"):
+                   "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo", "vinf_dual_domain_attn_clip",
+                   "vinf_groupnorm_stats", "vinf_temporal_conv3_gn"):
             getattr(L, fn).restype = ctypes.c_int
         L.vinf_status_string.argtypes = [i]
         L.vinf_status_string.restype = ctypes.c_char_p
@@ -212,21 +223,78 @@ def groupnorm_clip_sums(x: torch.Tensor, groups: int, F_total: int, mean_sums: t
 def groupnorm_clip_apply(x: torch.Tensor, groups: int, F_total: int, sums: torch.Tensor, sq_sums: torch.Tensor,
                          eps: float = 1e-5, gamma: torch.Tensor | None = None, beta: torch.Tensor | None = None,
                          out: torch.Tensor | None = None, mean_out: torch.Tensor | None = None,
-                         rstd_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
-    """Normalise one clip with the statistics of the all-clip sums.  Returns (y, mean, rstd)."""
+                         rstd_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         stats_only: bool = False, stream=None):
+    """Normalise one clip with the statistics of the all-clip sums.  Returns (y, mean, rstd);
+    with stats_only=True only the statistics are computed (y is None)."""
     _dev(x, "x")
     F, H, W, C = _fhwc(x)
     _f64(sums, "sums", groups)
     _f64(sq_sums, "sq_sums", groups)
-    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    y = None if stats_only else (torch.empty_like(x) if out is None else _dev(out, "out"))
     mean = torch.empty(groups, device=x.device, dtype=torch.float32) if mean_out is None else mean_out
     rstd = torch.empty(groups, device=x.device, dtype=torch.float32) if rstd_out is None else rstd_out
     workspace, ws_bytes = _workspace(x, groups, workspace)
-    st = load().vinf_groupnorm_clip_apply(_ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(sums), _ptr(sq_sums),
-                                           _ptr(mean), _ptr(rstd), F, H, W, C, groups, int(F_total), float(eps),
-                                           _dtype_code(x), _ptr(workspace), ws_bytes, _stream(x.device, stream))
+    st = load().vinf_groupnorm_clip_apply(None if stats_only else _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta),
+                                           _ptr(sums), _ptr(sq_sums), _ptr(mean), _ptr(rstd), F, H, W, C, groups,
+                                           int(F_total), float(eps), _dtype_code(x), _ptr(workspace), ws_bytes,
+                                           _stream(x.device, stream))
     _check("vinf_groupnorm_clip_apply", st)
     return y, mean, rstd
+
+
+def groupnorm_stats(x: torch.Tensor, groups: int, eps: float = 1e-5, mean_out: torch.Tensor | None = None,
+                    rstd_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Whole-video GroupNorm statistics only (the two sweeps).  Returns (mean[groups], rstd[groups])."""
+    _dev(x, "x")
+    F, H, W, C = _fhwc(x)
+    mean = torch.empty(groups, device=x.device, dtype=torch.float32) if mean_out is None else mean_out
+    rstd = torch.empty(groups, device=x.device, dtype=torch.float32) if rstd_out is None else rstd_out
+    workspace, ws_bytes = _workspace(x, groups, workspace)
+    st = load().vinf_groupnorm_stats(_ptr(x), _ptr(mean), _ptr(rstd), F, H, W, C, groups, float(eps), _dtype_code(x),
+                                     _ptr(workspace), ws_bytes, _stream(x.device, stream))
+    _check("vinf_groupnorm_stats", st)
+    return mean, rstd
+
+
+def temporal_conv3_gn_workspace_bytes(C: int, dtype: torch.dtype) -> int:
+    return int(load().vinf_temporal_conv3_gn_workspace_bytes(C, VINF_BF16 if dtype == torch.bfloat16 else VINF_F32))
+
+
+def temporal_conv3_gn(x: torch.Tensor, weight: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor,
+                      gamma: torch.Tensor | None = None, beta: torch.Tensor | None = None,
+                      ctx_pre: torch.Tensor | None = None, ctx_post: torch.Tensor | None = None,
+                      bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """conv3(GroupNorm(x)) with the given statistics (mean, rstd: float32 [groups]); x and
+    the context frames are raw (not normalised).  Bit for bit groupnorm apply + temporal_conv3."""
+    _dev(x, "x")
+    _dev(weight, "weight")
+    F, H, W, C = _fhwc(x)
+    if tuple(weight.shape) != (3, C, C) or weight.dtype != x.dtype:
+        raise ValueError(f"weight must be [3,{C},{C}] of {x.dtype}")
+    for name, c in (("ctx_pre", ctx_pre), ("ctx_post", ctx_post)):
+        if c is not None:
+            _dev(c, name)
+            if c.numel() != H * W * C or c.dtype != x.dtype:
+                raise ValueError(f"{name} must hold [H,W,C] = {H * W * C} values of {x.dtype}")
+    for name, v in (("mean", mean), ("rstd", rstd)):
+        _dev(v, name)
+        if v.dtype != torch.float32 or v.dim() != 1:
+            raise ValueError(f"{name} must be float32 [groups]")
+    groups = int(mean.numel())
+    if rstd.numel() != groups:
+        raise ValueError("mean and rstd must have the same length")
+    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    need = temporal_conv3_gn_workspace_bytes(C, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().vinf_temporal_conv3_gn(_ptr(x), _ptr(ctx_pre), _ptr(ctx_post), _ptr(weight), _ptr(bias), _ptr(mean),
+                                       _ptr(rstd), _ptr(gamma), _ptr(beta), groups, _ptr(y), F, H, W, C,
+                                       _dtype_code(x), _ptr(workspace), ws_bytes, _stream(x.device, stream))
+    _check("vinf_temporal_conv3_gn", st)
+    return y
 
 
 def dda_clip_halo(F_total: int, f0: int, Fc: int, n_local: int = 16) -> tuple[int, int]:

@@ -136,11 +136,40 @@ vinf_status vinf_groupnorm_global(const void* x, void* y, const float* gamma, co
                             (hipStream_t)stream);
 }
 
-// Shared checks of the two clip GroupNorm calls.
-static vinf_status check_gn_clip(const char* fn, const void* x, int F, int H, int W, int C, int groups, int F_total,
-                                 vinf_dtype dt, void* workspace, size_t workspace_bytes, size_t* bytes, size_t* need) {
-    VINF_TRY(check_shape(fn, F, H, W, C, dt, bytes));
+vinf_status vinf_groupnorm_stats(const void* x, float* mean_out, float* rstd_out, int F, int H, int W, int C,
+                                 int groups, float eps, vinf_dtype dt, void* workspace, size_t workspace_bytes,
+                                 vinf_stream stream) {
+    const char* fn = "vinf_groupnorm_stats";
+    size_t bytes;
+    VINF_TRY(check_shape(fn, F, H, W, C, dt, &bytes));
     VINF_TRY(check_tensor(fn, "x", x, true));
+    if (!mean_out || !rstd_out) return fail(VINF_ERR_INVALID_ARG, "%s: mean_out and rstd_out are required", fn);
+    VINF_TRY(check_f32(fn, "mean_out", mean_out));
+    VINF_TRY(check_f32(fn, "rstd_out", rstd_out));
+    if (groups < 1 || C % groups) return fail(VINF_ERR_INVALID_ARG, "%s: C=%d not divisible by groups=%d", fn, C, groups);
+    if (!(eps >= 0.f)) return fail(VINF_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+    const int vec = dt == VINF_BF16 ? 8 : 4;
+    if (C / vec > 1024) return fail(VINF_ERR_UNSUPPORTED, "%s: C=%d exceeds %d", fn, C, 1024 * vec);
+    const size_t need = groupnorm_workspace((int64_t)F * H * W, C, groups, dt);
+    if (!workspace || workspace_bytes < need)
+        return fail(VINF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(VINF_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", fn);
+    const size_t sb = (size_t)groups * sizeof(float);
+    if (overlap(workspace, need, x, bytes) || overlap(mean_out, sb, x, bytes) || overlap(rstd_out, sb, x, bytes) ||
+        overlap(workspace, need, mean_out, sb) || overlap(workspace, need, rstd_out, sb) ||
+        overlap(mean_out, sb, rstd_out, sb))
+        return fail(VINF_ERR_INVALID_ARG, "%s: workspace / statistics overlap", fn);
+    return launch_groupnorm(x, nullptr, nullptr, nullptr, mean_out, rstd_out, (int64_t)F * H * W, C, groups, eps, dt,
+                            workspace, (hipStream_t)stream);
+}
+
+// Shared checks of the two clip GroupNorm calls.
+static vinf_status check_gn_clip(const char* fn, const void* x, bool need_x, int F, int H, int W, int C, int groups,
+                                 int F_total, vinf_dtype dt, void* workspace, size_t workspace_bytes, size_t* bytes,
+                                 size_t* need) {
+    VINF_TRY(check_shape(fn, F, H, W, C, dt, bytes));
+    VINF_TRY(check_tensor(fn, "x", x, need_x));
     if (groups < 1 || C % groups) return fail(VINF_ERR_INVALID_ARG, "%s: C=%d not divisible by groups=%d", fn, C, groups);
     if (F_total < F) return fail(VINF_ERR_INVALID_ARG, "%s: F_total=%d is smaller than the clip's F=%d", fn, F_total, F);
     const int vec = dt == VINF_BF16 ? 8 : 4;
@@ -159,7 +188,7 @@ vinf_status vinf_groupnorm_clip_sums(const void* x, const double* mean_sums, dou
                                      vinf_stream stream) {
     const char* fn = "vinf_groupnorm_clip_sums";
     size_t bytes, need;
-    VINF_TRY(check_gn_clip(fn, x, F, H, W, C, groups, F_total, dt, workspace, workspace_bytes, &bytes, &need));
+    VINF_TRY(check_gn_clip(fn, x, true, F, H, W, C, groups, F_total, dt, workspace, workspace_bytes, &bytes, &need));
     VINF_TRY(check_f64(fn, "mean_sums", mean_sums, false));
     VINF_TRY(check_f64(fn, "sums", sums, true));
     const size_t sb = (size_t)groups * sizeof(double);
@@ -176,8 +205,14 @@ vinf_status vinf_groupnorm_clip_apply(const void* x, void* y, const float* gamma
                                       size_t workspace_bytes, vinf_stream stream) {
     const char* fn = "vinf_groupnorm_clip_apply";
     size_t bytes, need;
-    VINF_TRY(check_gn_clip(fn, x, F, H, W, C, groups, F_total, dt, workspace, workspace_bytes, &bytes, &need));
-    VINF_TRY(check_tensor(fn, "y", y, true));
+    // x == y == NULL: only the statistics (mean_out and rstd_out then required)
+    const bool stats_only = !x && !y;
+    if (stats_only && (!mean_out || !rstd_out))
+        return fail(VINF_ERR_INVALID_ARG, "%s: without x and y, mean_out and rstd_out are required", fn);
+    VINF_TRY(check_gn_clip(fn, x, !stats_only, F, H, W, C, groups, F_total, dt, workspace, workspace_bytes, &bytes,
+                           &need));
+    if (stats_only) bytes = 0;
+    VINF_TRY(check_tensor(fn, "y", y, !stats_only));
     VINF_TRY(check_f32(fn, "gamma", gamma));
     VINF_TRY(check_f32(fn, "beta", beta));
     VINF_TRY(check_f32(fn, "mean_out", mean_out));
@@ -192,6 +227,7 @@ vinf_status vinf_groupnorm_clip_apply(const void* x, void* y, const float* gamma
         overlap(rstd_out, st, x, bytes) || overlap(rstd_out, st, y, bytes) || overlap(workspace, need, mean_out, st) ||
         overlap(workspace, need, rstd_out, st))
         return fail(VINF_ERR_INVALID_ARG, "%s: workspace / statistics overlap a tensor", fn);
+    if (overlap(mean_out, st, rstd_out, st)) return fail(VINF_ERR_INVALID_ARG, "%s: mean_out overlaps rstd_out", fn);
     const double n_total = (double)F_total * H * W * (C / groups);
     return launch_groupnorm_clip_apply(x, y, gamma, beta, sums, sq_sums, mean_out, rstd_out, (int64_t)F * H * W, C,
                                        groups, n_total, eps, dt, workspace, (hipStream_t)stream);
@@ -217,6 +253,55 @@ vinf_status vinf_temporal_conv3(const void* x, const void* ctx_pre, const void* 
         overlap(y, bytes, ctx_post, cbytes) || overlap(y, bytes, bias, (size_t)C * 4))
         return fail(VINF_ERR_INVALID_ARG, "%s: y overlaps an input", fn);
     return launch_conv3(x, ctx_pre, ctx_post, weight, bias, y, F, H * W, C, dt, (hipStream_t)stream);
+}
+
+size_t vinf_temporal_conv3_gn_workspace_bytes(int C, vinf_dtype dt) {
+    if (C < 1 || (dt != VINF_F32 && dt != VINF_BF16)) return 0;
+    return conv3_gn_workspace(C, dt);
+}
+
+vinf_status vinf_temporal_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
+                                   const float* bias, const float* mean, const float* rstd, const float* gamma,
+                                   const float* beta, int groups, void* y, int F, int H, int W, int C,
+                                   vinf_dtype dt, void* workspace, size_t workspace_bytes, vinf_stream stream) {
+    const char* fn = "vinf_temporal_conv3_gn";
+    size_t bytes;
+    VINF_TRY(check_shape(fn, F, H, W, C, dt, &bytes));
+    VINF_TRY(check_tensor(fn, "x", x, true));
+    VINF_TRY(check_tensor(fn, "y", y, true));
+    VINF_TRY(check_tensor(fn, "weight", weight, true));
+    VINF_TRY(check_tensor(fn, "ctx_pre", ctx_pre, false));
+    VINF_TRY(check_tensor(fn, "ctx_post", ctx_post, false));
+    VINF_TRY(check_f32(fn, "bias", bias));
+    VINF_TRY(check_f32(fn, "gamma", gamma));
+    VINF_TRY(check_f32(fn, "beta", beta));
+    if (!mean || !rstd) return fail(VINF_ERR_INVALID_ARG, "%s: mean and rstd are required", fn);
+    VINF_TRY(check_f32(fn, "mean", mean));
+    VINF_TRY(check_f32(fn, "rstd", rstd));
+    if (groups < 1 || C % groups) return fail(VINF_ERR_INVALID_ARG, "%s: C=%d not divisible by groups=%d", fn, C, groups);
+    if (dt == VINF_BF16 && C % 32)
+        return fail(VINF_ERR_UNSUPPORTED, "%s: bf16 needs C %% 32 == 0 (MFMA tiles), got C=%d", fn, C);
+    const size_t need = conv3_gn_workspace(C, dt);
+    if (!workspace || workspace_bytes < need)
+        return fail(VINF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(VINF_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", fn);
+    const size_t wbytes = (size_t)3 * C * C * dtype_bytes(dt);
+    const size_t cbytes = (size_t)H * W * C * dtype_bytes(dt);
+    const size_t gb = (size_t)groups * sizeof(float), vb = (size_t)C * sizeof(float);
+    const struct {
+        const void* p;
+        size_t n;
+    } in[] = {{x, bytes}, {ctx_pre, cbytes}, {ctx_post, cbytes}, {weight, wbytes}, {bias, vb},
+              {mean, gb}, {rstd, gb}, {gamma, vb}, {beta, vb}};
+    for (const auto& r : in) {
+        if (overlap(y, bytes, r.p, r.n)) return fail(VINF_ERR_INVALID_ARG, "%s: y overlaps an input", fn);
+        if (overlap(workspace, need, r.p, r.n))
+            return fail(VINF_ERR_INVALID_ARG, "%s: the workspace overlaps an input", fn);
+    }
+    if (overlap(workspace, need, y, bytes)) return fail(VINF_ERR_INVALID_ARG, "%s: the workspace overlaps y", fn);
+    return launch_conv3_gn(x, ctx_pre, ctx_post, weight, bias, mean, rstd, gamma, beta, groups, y, F, H * W, C, dt,
+                           workspace, (hipStream_t)stream);
 }
 
 // Shared checks of the attention calls: head layout and key-set sizes.

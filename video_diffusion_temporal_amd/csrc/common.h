@@ -63,6 +63,7 @@ inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 inline size_t dtype_bytes(vinf_dtype dt) { return dt == VINF_BF16 ? 2 : 4; }
 
 // Launchers implemented next to their kernels (arguments already validated).
+// y == NULL: statistics only (the two sweeps; mean_out and rstd_out required).
 vinf_status launch_groupnorm(const void* x, void* y, const float* gamma, const float* beta, float* mean_out,
                              float* rstd_out, int64_t rows, int C, int groups, float eps, vinf_dtype dt,
                              void* workspace, hipStream_t stream);
@@ -72,7 +73,8 @@ size_t groupnorm_workspace(int64_t rows, int C, int groups, vinf_dtype dt);
 vinf_status launch_groupnorm_clip_sums(const void* x, const double* mean_sums, double* sums, int64_t rows, int C,
                                        int groups, double n_total, vinf_dtype dt, void* workspace,
                                        hipStream_t stream);
-// Normalise one clip with the statistics of the aggregated sums.
+// Normalise one clip with the statistics of the aggregated sums (x == NULL:
+// statistics only).
 vinf_status launch_groupnorm_clip_apply(const void* x, void* y, const float* gamma, const float* beta,
                                         const double* sums, const double* sq_sums, float* mean_out, float* rstd_out,
                                         int64_t rows, int C, int groups, double n_total, float eps, vinf_dtype dt,
@@ -80,6 +82,13 @@ vinf_status launch_groupnorm_clip_apply(const void* x, void* y, const float* gam
 
 vinf_status launch_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
                          const float* bias, void* y, int F, int S, int C, vinf_dtype dt, hipStream_t stream);
+// The conv of GroupNorm(x) with the given statistics, the normalisation
+// applied to the conv's input tiles (workspace: conv3_gn_workspace bytes).
+size_t conv3_gn_workspace(int C, vinf_dtype dt);
+vinf_status launch_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
+                            const float* bias, const float* mean, const float* rstd, const float* gamma,
+                            const float* beta, int groups, void* y, int F, int S, int C, vinf_dtype dt,
+                            void* workspace, hipStream_t stream);
 
 // Attention of query frames f0 .. f0+nq-1 of an F-frame video; k/v hold
 // frames kf0 .. kend-1; kg/vg the global rows or null (read from k/v).

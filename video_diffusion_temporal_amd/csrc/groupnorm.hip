@@ -301,7 +301,7 @@ static vinf_status run(const void* x, void* y, const float* gamma, const float* 
     sweep<BF16, true>(x, b, rows, C, cpg, st);
     hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(256), 0, st, b.partial, b.stats, rstd_out, nullptr,
                        b.g.blocks, C, cpg, G, n, eps);
-    apply<BF16>(x, y, gamma, beta, b, rows, C, cpg, G, st);
+    if (y) apply<BF16>(x, y, gamma, beta, b, rows, C, cpg, G, st);
     return check_launch("groupnorm");
 }
 
@@ -331,7 +331,7 @@ static vinf_status run_clip_apply(const void* x, void* y, const float* gamma, co
     const GnBufs b = gn_bufs(rows, C, BF16 ? VINF_BF16 : VINF_F32, ws);
     hipLaunchKernelGGL(gn_stats_from_sums, dim3((G + 255) / 256), dim3(256), 0, st, sums, sq_sums, b.stats, mean_out,
                        rstd_out, G, n_total, eps);
-    apply<BF16>(x, y, gamma, beta, b, rows, C, C / G, G, st);
+    if (x) apply<BF16>(x, y, gamma, beta, b, rows, C, C / G, G, st);
     return check_launch("groupnorm_clip_apply");
 }
 

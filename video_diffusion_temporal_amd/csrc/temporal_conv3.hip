@@ -38,6 +38,19 @@
 //     barrier per slice, and the next slice's loads are in flight while the
 //     current one is multiplied.
 // fp32 kernel (conv3_f32): one output element per thread, fp32 FMA.
+//
+// GroupNorm applied inside the conv (conv3_bf16<.., GN = true>, conv3_f32
+// with gn tables): the GroupNorm output g = x*a_c + b_c (a_c = rstd_g*gamma_c,
+// b_c = beta_c - mean_g*a_c, formed in fp32 exactly as the GroupNorm apply
+// forms them) is what the conv multiplies, but it is never written to HBM.
+// In the bf16 kernel each x slice lands in LDS raw (DMA); every wave then
+// rewrites the frame blocks its own loads filled, in place, as
+// fmaf(x, a_c, b_c) rounded to bf16, before the slice's one barrier.  Each lane's 16-byte slot
+// of a block always holds the same 8 channels of the slice, so a lane needs
+// 8 (a, b) pairs per slice, loaded while the previous slice is multiplied.
+// Zero pads stay zero (they are zeros of the normalised tensor); context
+// frames are raw neighbouring frames and are normalised like the rest.  The
+// result is bit for bit that of the GroupNorm apply followed by the conv.
 #include <algorithm>
 
 #include "common.h"
@@ -63,11 +76,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t cv_rsrc(const void* base, uint
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int NF, int WN>
+template <int NF, int WN, bool GN>
 __global__ void __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(WN, WN)))
 conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, const uint16_t* __restrict__ post,
-           const uint16_t* __restrict__ w, const float* __restrict__ bias, uint16_t* __restrict__ y, int F, int S,
-           int C, int nfb, int nlb, int ntn) {
+           const uint16_t* __restrict__ w, const float* __restrict__ bias, const float* __restrict__ gn_a,
+           const float* __restrict__ gn_b, uint16_t* __restrict__ y, int F, int S, int C, int nfb, int nlb,
+           int ntn) {
     using L = ConvLds<NF, WN>;
     constexpr int BN = L::BN;
     constexpr int NW = 4 * WN;                  // waves: 4 along M x WN along N
@@ -141,12 +155,52 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 #pragma unroll
         for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (t_begin < t_end) issue(t_begin, 0, 0);
+    // GroupNorm coefficients of the lane's 8 channels of slice kc (its LDS
+    // slot in every frame block holds chunk st_chunk of the slice).
+    f32x4_t gna[2], gnb[2];
+    auto gn_load = [&](int kc) {
+        if constexpr (GN) {
+            const int c0 = kc * CV_BK + st_chunk * 8;
+            gna[0] = *reinterpret_cast<const f32x4_t*>(gn_a + c0);
+            gna[1] = *reinterpret_cast<const f32x4_t*>(gn_a + c0 + 4);
+            gnb[0] = *reinterpret_cast<const f32x4_t*>(gn_b + c0);
+            gnb[1] = *reinterpret_cast<const f32x4_t*>(gn_b + c0 + 4);
+        }
+    };
+    // Normalise, in place, the frame blocks of the landed x slice that this
+    // wave's own loads filled (the blocks issue() gives it).  Zero pads are
+    // zeros of the normalised tensor and stay as they are.
+    auto gn_apply_tile = [&](int t, char* abuf) {
+        int f0, s0, n0;
+        tile_coords(t, f0, s0, n0);
+        for (int i = wv; i < CV_TF + 2; i += NW) {
+            const int f = f0 - 1 + i;
+            if (!((f >= 0 && f < F) || (f == -1 && pre) || (f == F && post))) continue;
+            u32x4_t* p = reinterpret_cast<u32x4_t*>(abuf + i * 1024 + lane * 16);
+            const u32x4_t u = *p;
+            u32x4_t v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = fmaf(bf_lo(u[j]), gna[j >> 1][2 * (j & 1)], gnb[j >> 1][2 * (j & 1)]);
+                const float hi = fmaf(bf_hi(u[j]), gna[j >> 1][2 * (j & 1) + 1], gnb[j >> 1][2 * (j & 1) + 1]);
+                v[j] = pack_bf16x2(lo, hi);
+            }
+            *p = v;
+        }
+    };
+
+    if (t_begin < t_end) {
+        issue(t_begin, 0, 0);
+        gn_load(0);
+    }
     int g = 0;  // slice counter across tiles (selects the buffer)
     for (int t = t_begin; t < t_end; ++t) {
         for (int kc = 0; kc < nk; ++kc, ++g) {
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of slice g are in LDS
-            __syncthreads();                      // everyone's are; slice g-1 is no longer read
+            // Each wave normalises the frame blocks its own loads filled (the
+            // same blocks issue() gives it), so its own vmcnt wait suffices.
+            if constexpr (GN) gn_apply_tile(t, lds + (g & 1) * L::BUF);
+            __syncthreads();                      // everyone's are (normalised); slice g-1 is no longer read
             if (kc + 1 < nk)
                 issue(t, kc + 1, (g + 1) & 1);
             else if (t + 1 < t_end)
@@ -183,6 +237,8 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 if (gi + LA < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            // the next slice's GroupNorm coefficients, in flight over the wait at the loop top
+            if constexpr (GN) gn_load(kc + 1 < nk ? kc + 1 : 0);
         }
         // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, location
         // s0 + lane%16, channels n0 + wn*16*NF + ni*16 + 4*(lane/16) + 0..3.
@@ -215,10 +271,13 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 }
 
 // float32 I/O: one output element per thread.
+// With gn_a / gn_b (GroupNorm applied inside) each input value is first
+// fmaf(x, a_ci, b_ci), as the GroupNorm apply writes it.
 __global__ void __launch_bounds__(256) conv3_f32(const float* __restrict__ x, const float* __restrict__ pre,
                                                  const float* __restrict__ post, const float* __restrict__ w,
-                                                 const float* __restrict__ bias, float* __restrict__ y, int F, int S,
-                                                 int C) {
+                                                 const float* __restrict__ bias, const float* __restrict__ gn_a,
+                                                 const float* __restrict__ gn_b, float* __restrict__ y, int F,
+                                                 int S, int C) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)F * S * C) return;
     const int co = (int)(idx % C);
@@ -237,9 +296,28 @@ __global__ void __launch_bounds__(256) conv3_f32(const float* __restrict__ x, co
             xr = x + ((int64_t)fs * S + s) * C;
         if (!xr) continue;
         const float* wr = w + ((int64_t)k * C + co) * C;
-        for (int ci = 0; ci < C; ++ci) acc = fmaf(wr[ci], xr[ci], acc);
+        if (gn_a)
+            for (int ci = 0; ci < C; ++ci) acc = fmaf(wr[ci], fmaf(xr[ci], gn_a[ci], gn_b[ci]), acc);
+        else
+            for (int ci = 0; ci < C; ++ci) acc = fmaf(wr[ci], xr[ci], acc);
     }
     y[idx] = acc;
+}
+
+// The GroupNorm coefficients per channel, in fp32 exactly as the GroupNorm
+// apply forms them: a_c = rstd_g * gamma_c, b_c = beta_c - mean_g * a_c.
+__global__ void __launch_bounds__(256) conv3_gn_coeffs(const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                       const float* __restrict__ gamma,
+                                                       const float* __restrict__ beta, int C, int cpg,
+                                                       float* __restrict__ a, float* __restrict__ b) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
+    const int g = c / cpg;
+    const float ga = gamma ? gamma[c] : 1.f;
+    const float be = beta ? beta[c] : 0.f;
+    const float ac = rstd[g] * ga;
+    a[c] = ac;
+    b[c] = be - mean[g] * ac;
 }
 
 }  // namespace vinf
@@ -249,7 +327,7 @@ using namespace vinf;
 
 template <int NF, int WN>
 static vinf_status launch_bf16(const void* x, const void* pre, const void* post, const void* w, const float* bias,
-                               void* y, int F, int S, int C, hipStream_t st) {
+                               const float* gn_a, const float* gn_b, void* y, int F, int S, int C, hipStream_t st) {
     const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP, ntn = C / ConvLds<NF, WN>::BN;
     const int64_t tiles = (int64_t)nfb * nlb * ntn;
     if (tiles > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: too many tiles");
@@ -259,26 +337,34 @@ static vinf_status launch_bf16(const void* x, const void* pre, const void* post,
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return fail(VINF_ERR_HIP, "temporal_conv3: cannot query the device");
     const int grid = (int)std::min<int64_t>(cus, tiles);
-    hipLaunchKernelGGL((conv3_bf16<NF, WN>), dim3(grid), dim3(256 * WN), 0, st, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(pre), static_cast<const uint16_t*>(post),
-                       static_cast<const uint16_t*>(w), bias, static_cast<uint16_t*>(y), F, S, C, nfb, nlb, ntn);
+    const uint16_t *xb = static_cast<const uint16_t*>(x), *pb = static_cast<const uint16_t*>(pre),
+                   *qb = static_cast<const uint16_t*>(post), *wb = static_cast<const uint16_t*>(w);
+    uint16_t* yb = static_cast<uint16_t*>(y);
+    if (gn_a)
+        hipLaunchKernelGGL((conv3_bf16<NF, WN, true>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias, gn_a,
+                           gn_b, yb, F, S, C, nfb, nlb, ntn);
+    else
+        hipLaunchKernelGGL((conv3_bf16<NF, WN, false>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias,
+                           gn_a, gn_b, yb, F, S, C, nfb, nlb, ntn);
     return VINF_OK;
 }
 
-vinf_status launch_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
-                         const float* bias, void* y, int F, int S, int C, vinf_dtype dt, hipStream_t st) {
+// The conv, with the GroupNorm coefficient tables gn_a / gn_b or without (null).
+static vinf_status run_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
+                             const float* bias, const float* gn_a, const float* gn_b, void* y, int F, int S, int C,
+                             vinf_dtype dt, hipStream_t st) {
     if (dt == VINF_BF16) {
         vinf_status r;
         if (C % 320 == 0)
-            r = launch_bf16<5, 4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<5, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
         else if (C % 256 == 0)
-            r = launch_bf16<4, 4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<4, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
         else if (C % 128 == 0)
-            r = launch_bf16<2, 4>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<2, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
         else if (C % 64 == 0)
-            r = launch_bf16<2, 2>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<2, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
         else
-            r = launch_bf16<1, 2>(x, ctx_pre, ctx_post, weight, bias, y, F, S, C, st);
+            r = launch_bf16<1, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
         if (r != VINF_OK) return r;
     } else {
         const int64_t n = (int64_t)F * S * C;
@@ -286,9 +372,36 @@ vinf_status launch_conv3(const void* x, const void* ctx_pre, const void* ctx_pos
         if (blocks > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: grid too large");
         hipLaunchKernelGGL(conv3_f32, dim3((uint32_t)blocks), dim3(256), 0, st, static_cast<const float*>(x),
                            static_cast<const float*>(ctx_pre), static_cast<const float*>(ctx_post),
-                           static_cast<const float*>(weight), bias, static_cast<float*>(y), F, S, C);
+                           static_cast<const float*>(weight), bias, gn_a, gn_b, static_cast<float*>(y), F, S, C);
     }
+    return VINF_OK;
+}
+
+vinf_status launch_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
+                         const float* bias, void* y, int F, int S, int C, vinf_dtype dt, hipStream_t st) {
+    const vinf_status r = run_conv3(x, ctx_pre, ctx_post, weight, bias, nullptr, nullptr, y, F, S, C, dt, st);
+    if (r != VINF_OK) return r;
     return check_launch("temporal_conv3");
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+size_t conv3_gn_workspace(int C, vinf_dtype dt) {
+    (void)dt;
+    return 2 * align256((size_t)C * sizeof(float));
+}
+
+vinf_status launch_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
+                            const float* bias, const float* mean, const float* rstd, const float* gamma,
+                            const float* beta, int groups, void* y, int F, int S, int C, vinf_dtype dt,
+                            void* workspace, hipStream_t st) {
+    float* a = static_cast<float*>(workspace);
+    float* b = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)C * sizeof(float)));
+    hipLaunchKernelGGL(conv3_gn_coeffs, dim3((C + 255) / 256), dim3(256), 0, st, mean, rstd, gamma, beta, C,
+                       C / groups, a, b);
+    const vinf_status r = run_conv3(x, ctx_pre, ctx_post, weight, bias, a, b, y, F, S, C, dt, st);
+    if (r != VINF_OK) return r;
+    return check_launch("temporal_conv3_gn");
 }
 
 }  // namespace vinf_host
