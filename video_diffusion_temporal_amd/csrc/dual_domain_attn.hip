@@ -28,6 +28,10 @@
 //     is the sum of the same bf16-rounded weights, so the output is an exact
 //     convex combination of the V rows up to fp32 rounding.
 //   * Output: fp32 -> bf16 (nearest even), 128-byte row per lane.
+//   * Remainders: when the query count leaves r = nq % 256 queries per strip
+//     (a clip of 288 frames: 32), M strips share one item (M = 4 for r <= 36,
+//     2 for r <= 104), each in its own slice of the buffer with 4/M waves, so
+//     a short remainder does not cost a whole item per strip.
 //   * Pipelining: one persistent 512-thread workgroup per CU owns two LDS
 //     buffers (2 x 80 KB).  Its two 256-thread halves alternate: while one
 //     half stages its next work item (HBM -> LDS, plus its q rows into
@@ -39,6 +43,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -47,17 +52,34 @@ namespace vinf {
 constexpr int DDA_D = 64;          // head dim
 constexpr int DDA_L = 16;          // local keys
 constexpr int DDA_G = 16;          // global keys
-constexpr int DDA_TQ = 256;        // queries per workgroup
-constexpr int DDA_KROWS = DDA_TQ + DDA_L - 1;        // 271 local K rows
-constexpr int DDA_VPAIRS = (DDA_TQ + 18) / 2;        // 137 local V pair rows
-constexpr int DDA_KSTR = 144;                        // padded K row (bytes)
-constexpr int DDA_VSTR = 272;                        // padded V pair row (bytes)
-constexpr int DDA_LDS_KG = 0;                        // 16 global K rows, 128 B
-constexpr int DDA_LDS_VG = DDA_LDS_KG + DDA_G * 128; // 8 global V pair rows, 256 B
-constexpr int DDA_LDS_KL = DDA_LDS_VG + (DDA_G / 2) * 256;
-constexpr int DDA_LDS_VP = DDA_LDS_KL + DDA_KROWS * DDA_KSTR;
-constexpr int DDA_LDS_BYTES = DDA_LDS_VP + DDA_VPAIRS * DDA_VSTR;
-static_assert(2 * DDA_LDS_BYTES <= 160 * 1024, "two workgroups per CU");
+constexpr int DDA_TQ = 256;        // queries per work item (one per thread of a half workgroup)
+constexpr int DDA_KSTR = 144;      // padded K row (bytes)
+constexpr int DDA_VSTR = 272;      // padded V pair row (bytes)
+
+// LDS slice of one strip for up to R consecutive queries: 16 global K rows
+// (128 B), 8 global V pair rows (256 B), then the R + 15 local K rows and
+// (R + 18) / 2 local V pair rows their windows cover.
+template <int R>
+struct DdaSlice {
+    static constexpr int KROWS = R + DDA_L - 1;
+    static constexpr int VPAIRS = (R + 18) / 2;
+    static constexpr int KG = 0;
+    static constexpr int VG = KG + DDA_G * 128;
+    static constexpr int KL = VG + (DDA_G / 2) * 256;
+    static constexpr int VP = KL + KROWS * DDA_KSTR;
+    static constexpr int BYTES = VP + VPAIRS * DDA_VSTR;
+};
+using DdaFull = DdaSlice<DDA_TQ>;
+constexpr int DDA_LDS_BYTES = DdaFull::BYTES;  // one half workgroup's buffer
+static_assert(2 * DDA_LDS_BYTES <= 160 * 1024, "two buffers per CU");
+
+// Remainder items: when a clip's query count leaves r = nq % 256 queries per
+// strip, M strips share one item (4 / M waves each, up to DdaRemR<M> queries
+// per strip), each in its own slice of the half's buffer.
+template <int M>
+constexpr int DdaRemR = M == 4 ? 36 : (M == 2 ? 104 : DDA_TQ);
+static_assert(4 * DdaSlice<DdaRemR<4>>::BYTES <= DDA_LDS_BYTES, "4 remainder slices");
+static_assert(2 * DdaSlice<DdaRemR<2>>::BYTES <= DDA_LDS_BYTES, "2 remainder slices");
 
 __device__ __forceinline__ int dda_start(int t, int F) {
     int hi = F - DDA_L > 0 ? F - DDA_L : 0;
@@ -73,11 +95,13 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __b
 // kf0 .. kend-1 (row 0 is frame kf0).  kg and vg hold the global rows (row i
 // is frame floor(i*F/16)) or are null when k and v hold those frames.  The
 // whole video on its own is f0 = kf0 = 0, nq = kend = F, kg = vg = null.
+// Work items: nfull = nstrips * nchunks items of (strip, 256 query frames
+// from f0 + 256*chunk), then the remainder items (packed kernels only).
 struct DdaGeo {
     const void* kg;
     const void* vg;
     int F, f0, nq, kf0, kend;
-    int S, C, nstrips, nitems;
+    int S, C, nstrips, nchunks, nfull, nitems;
     float sl2e;
 };
 
@@ -85,17 +109,16 @@ struct DdaItem {
     int strip, t0;
 };
 
-__device__ __forceinline__ DdaItem dda_item(const DdaGeo& g, int idx) {
-    return DdaItem{idx % g.nstrips, g.f0 + (idx / g.nstrips) * DDA_TQ};
-}
-
-// Stage one work item into `buf` (256 threads, lt = 0..255) and load the q row
-// of query t0 + lt into qv.  NL / NG: local / global keys present (16 or 0).
-template <int NL, int NG>
+// Stage one strip's rows for queries t0 .. t0+R-1 into its slice `buf`
+// (NT threads, lt = 0..NT-1) and load the q row of query t0 + lt into qv.
+// NL / NG: local / global keys present (16 or 0).
+template <int NL, int NG, int R, int NT>
 __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t* __restrict__ q,
                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                           const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
                                           uint32_t (&qv)[32]) {
+    using SL = DdaSlice<R>;
+    constexpr int RSTEP = NT / 8;  // rows one pass of the threads covers (8 chunks per row)
     const int s = it.strip / heads, h = it.strip % heads;
     const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int t = it.t0 + lt;
@@ -111,90 +134,97 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
         }
     }
     if constexpr (NL > 0) {
-        const int tlast = min(it.t0 + DDA_TQ, g.f0 + g.nq) - 1;
+        const int tlast = min(it.t0 + R, g.f0 + g.nq) - 1;
         const int lo = dda_start(it.t0, g.F);
         const int stl = dda_start(tlast, g.F);
-        const int nkr = stl + DDA_L - lo;             // K rows [lo, lo+nkr), <= 271
+        const int nkr = stl + DDA_L - lo;             // K rows [lo, lo+nkr), <= R + 15
         const int plo = lo & ~1;
-        const int np = (stl + DDA_L + 2 - plo) >> 1;  // V pairs cover [plo, plo+2np), <= 137
+        const int np = (stl + DDA_L + 2 - plo) >> 1;  // V pairs cover [plo, plo+2np), <= (R + 18) / 2
         // Frames outside [kf0, kend) are not in k/v: their rows are zero-filled
         // (only frames past the video's last frame, or the unused half of a
         // pair row, which carry no weight, fall outside).
-        // local K rows: this thread's chunk c = lt&7 of rows lt>>3 + 32*i
+        // local K rows: this thread's chunk c = lt&7 of rows lt>>3 + RSTEP*i
         {
+            constexpr int NI = (SL::KROWS + RSTEP - 1) / RSTEP;
             const int c = lt & 7, r0 = lt >> 3;
             const uint16_t* src = k + col + (int64_t)(lo + r0 - g.kf0) * rs + c * 8;
-            char* dst = buf + DDA_LDS_KL + r0 * DDA_KSTR + c * 16;
-            u32x4_t u[(DDA_KROWS + 31) / 32];
+            char* dst = buf + SL::KL + r0 * DDA_KSTR + c * 16;
+            u32x4_t u[NI];
 #pragma unroll
-            for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i) {
-                const int r = r0 + 32 * i;
+            for (int i = 0; i < NI; ++i) {
+                const int r = r0 + RSTEP * i;
                 u[i] = u32x4_t{0u, 0u, 0u, 0u};
-                if (r < nkr && lo + r < g.kend) u[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(32 * i) * rs);
+                if (r < nkr && lo + r < g.kend)
+                    u[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(RSTEP * i) * rs);
             }
 #pragma unroll
-            for (int i = 0; i < (DDA_KROWS + 31) / 32; ++i)
-                if (r0 + 32 * i < nkr) *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_KSTR) = u[i];
+            for (int i = 0; i < NI; ++i)
+                if (r0 + RSTEP * i < nkr) *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_KSTR) = u[i];
         }
-        // local V as frame pairs: this thread's 8-dim group oc = lt&7 of pairs lt>>3 + 32*i
+        // local V as frame pairs: this thread's 8-dim group oc = lt&7 of pairs lt>>3 + RSTEP*i
         {
+            constexpr int NI = (SL::VPAIRS + RSTEP - 1) / RSTEP;
             const int oc = lt & 7, p0 = lt >> 3;
             const uint16_t* src = v + col + (int64_t)(plo + 2 * p0 - g.kf0) * rs + oc * 8;
-            char* dst = buf + DDA_LDS_VP + p0 * DDA_VSTR + oc * 32;
-            u32x4_t a[(DDA_VPAIRS + 31) / 32], b[(DDA_VPAIRS + 31) / 32];
+            char* dst = buf + SL::VP + p0 * DDA_VSTR + oc * 32;
+            u32x4_t a[NI], b[NI];
 #pragma unroll
-            for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
-                const int p = p0 + 32 * i, fa = plo + 2 * p;
+            for (int i = 0; i < NI; ++i) {
+                const int p = p0 + RSTEP * i, fa = plo + 2 * p;
                 a[i] = u32x4_t{0u, 0u, 0u, 0u};
                 b[i] = u32x4_t{0u, 0u, 0u, 0u};
                 if (p < np && fa >= g.kf0 && fa < g.kend)
-                    a[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i) * rs);
+                    a[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(2 * RSTEP * i) * rs);
                 if (p < np && fa + 1 < g.kend)
-                    b[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(64 * i + 1) * rs);
+                    b[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(2 * RSTEP * i + 1) * rs);
             }
 #pragma unroll
-            for (int i = 0; i < (DDA_VPAIRS + 31) / 32; ++i) {
-                if (p0 + 32 * i < np) {
+            for (int i = 0; i < NI; ++i) {
+                if (p0 + RSTEP * i < np) {
                     u32x4_t w0 = {perm_lo(a[i][0], b[i][0]), perm_hi(a[i][0], b[i][0]), perm_lo(a[i][1], b[i][1]),
                                   perm_hi(a[i][1], b[i][1])};
                     u32x4_t w1 = {perm_lo(a[i][2], b[i][2]), perm_hi(a[i][2], b[i][2]), perm_lo(a[i][3], b[i][3]),
                                   perm_hi(a[i][3], b[i][3])};
-                    *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR) = w0;
-                    *reinterpret_cast<u32x4_t*>(dst + 32 * i * DDA_VSTR + 16) = w1;
+                    *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_VSTR) = w0;
+                    *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_VSTR + 16) = w1;
                 }
             }
         }
     }
     if constexpr (NG > 0) {
-        // global K rows (threads 0..127) and V pairs (threads 128..191)
+        // 192 tasks: global K row chunks (tasks 0..127) and V pair chunks (128..191)
         const uint16_t* kgb = g.kg ? static_cast<const uint16_t*>(g.kg) : k;
         const uint16_t* vgb = g.vg ? static_cast<const uint16_t*>(g.vg) : v;
         auto grow = [&](int i) -> int64_t {  // row of global frame i in kgb / vgb
             return g.kg ? (int64_t)i : (int64_t)(((int64_t)i * g.F) / DDA_G) - g.kf0;
         };
-        if (lt < DDA_G * 8) {
-            const int i = lt >> 3, c = lt & 7;
-            *reinterpret_cast<u32x4_t*>(buf + DDA_LDS_KG + i * 128 + c * 16) =
-                *reinterpret_cast<const u32x4_t*>(kgb + col + grow(i) * rs + c * 8);
-        } else if (lt < DDA_G * 8 + (DDA_G / 2) * 8) {
-            const int j = lt - DDA_G * 8;
-            const int p = j >> 3, oc = j & 7;
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p) * rs + oc * 8);
-            const u32x4_t b = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p + 1) * rs + oc * 8);
-            u32x4_t w0 = {perm_lo(a[0], b[0]), perm_hi(a[0], b[0]), perm_lo(a[1], b[1]), perm_hi(a[1], b[1])};
-            u32x4_t w1 = {perm_lo(a[2], b[2]), perm_hi(a[2], b[2]), perm_lo(a[3], b[3]), perm_hi(a[3], b[3])};
-            char* dst = buf + DDA_LDS_VG + p * 256 + oc * 32;
-            *reinterpret_cast<u32x4_t*>(dst) = w0;
-            *reinterpret_cast<u32x4_t*>(dst + 16) = w1;
+#pragma unroll
+        for (int task = lt; task < DDA_G * 8 + (DDA_G / 2) * 8; task += NT) {
+            if (task < DDA_G * 8) {
+                const int i = task >> 3, c = task & 7;
+                *reinterpret_cast<u32x4_t*>(buf + SL::KG + i * 128 + c * 16) =
+                    *reinterpret_cast<const u32x4_t*>(kgb + col + grow(i) * rs + c * 8);
+            } else {
+                const int j = task - DDA_G * 8;
+                const int p = j >> 3, oc = j & 7;
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p) * rs + oc * 8);
+                const u32x4_t b = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p + 1) * rs + oc * 8);
+                u32x4_t w0 = {perm_lo(a[0], b[0]), perm_hi(a[0], b[0]), perm_lo(a[1], b[1]), perm_hi(a[1], b[1])};
+                u32x4_t w1 = {perm_lo(a[2], b[2]), perm_hi(a[2], b[2]), perm_lo(a[3], b[3]), perm_hi(a[3], b[3])};
+                char* dst = buf + SL::VG + p * 256 + oc * 32;
+                *reinterpret_cast<u32x4_t*>(dst) = w0;
+                *reinterpret_cast<u32x4_t*>(dst + 16) = w1;
+            }
         }
     }
 }
 
-// Compute query t0 + lt of a staged work item from `buf`.
-template <int NL, int NG>
+// Compute query t0 + lt of a strip staged in slice `buf` (layout DdaSlice<R>).
+template <int NL, int NG, int R>
 __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16_t* __restrict__ o,
                                             const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
                                             const uint32_t (&qv)[32]) {
+    using SL = DdaSlice<R>;
     constexpr int NK = NL + NG;                 // keys
     constexpr int NLP = NL > 0 ? 9 : 0;         // local V pair rows
     constexpr int NP = NLP + (NG > 0 ? 8 : 0);  // V pair rows
@@ -211,9 +241,9 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // ---- scores: one K row (8 x 16 B) per key; the next row's reads are
     // issued before the current row's dot products ----
     float sc[NK];
-    const char* krow = buf + DDA_LDS_KL + (st - lo) * DDA_KSTR;
+    const char* krow = buf + SL::KL + (st - lo) * DDA_KSTR;
     auto key_row = [&](int i) -> const char* {
-        return i < NL ? krow + i * DDA_KSTR : buf + DDA_LDS_KG + (i - NL) * 128;
+        return i < NL ? krow + i * DDA_KSTR : buf + SL::KG + (i - NL) * 128;
     };
     u32x4_t kb[2][8];
 #pragma unroll
@@ -273,9 +303,9 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     float acc[DDA_D];
 #pragma unroll
     for (int d = 0; d < DDA_D; ++d) acc[d] = 0.f;
-    const char* vrow = buf + DDA_LDS_VP + ((st - plo) >> 1) * DDA_VSTR;
+    const char* vrow = buf + SL::VP + ((st - plo) >> 1) * DDA_VSTR;
     auto val_row = [&](int j) -> const char* {
-        return j < NLP ? vrow + j * DDA_VSTR : buf + DDA_LDS_VG + (j - NLP) * 256;
+        return j < NLP ? vrow + j * DDA_VSTR : buf + SL::VG + (j - NLP) * 256;
     };
     // half rows (32 dims, 8 x 16 B) double-buffered: step 2j + hh reads
     // dims 32*hh.. of pair row j
@@ -311,13 +341,42 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     }
 }
 
+// One work item of a half workgroup (256 threads, lt = 0..255): stage it
+// (STAGE) or compute it.  Items below g.nfull are one strip x 256 queries;
+// the rest are remainder items of M strips (s0 .. s0+M-1) x the last
+// nq - 256*nchunks queries, strip j in slice j of the buffer, threads
+// 256/M*j .. 256/M*(j+1)-1 (waves 4/M*j ..) on it.
+template <int NL, int NG, int M, bool STAGE>
+__device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint16_t* __restrict__ q,
+                                             const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                             uint16_t* __restrict__ o, const DdaGeo& g, int64_t rs, int heads,
+                                             int idx, int lt, uint32_t (&qv)[32]) {
+    if (M == 1 || idx < g.nfull) {
+        const DdaItem it{idx % g.nstrips, g.f0 + (idx / g.nstrips) * DDA_TQ};
+        if constexpr (STAGE)
+            dda_stage<NL, NG, DDA_TQ, 256>(buf, q, k, v, g, rs, heads, it, lt, qv);
+        else
+            dda_compute<NL, NG, DDA_TQ>(buf, o, g, rs, heads, it, lt, qv);
+    } else {
+        constexpr int R = DdaRemR<M>, NT = 256 / M;
+        const int j = lt / NT, ls = lt % NT;
+        const DdaItem it{(idx - g.nfull) * M + j, g.f0 + g.nchunks * DDA_TQ};
+        if (it.strip >= g.nstrips) return;  // the last remainder item may hold fewer strips
+        char* slice = buf + j * DdaSlice<R>::BYTES;
+        if constexpr (STAGE)
+            dda_stage<NL, NG, R, NT>(slice, q, k, v, g, rs, heads, it, ls, qv);
+        else
+            dda_compute<NL, NG, R>(slice, o, g, rs, heads, it, ls, qv);
+    }
+}
+
 // Persistent, two-phase pipelined kernel: workgroup w takes items
 // w, w + G, w + 2G, ... (G = gridDim.x); its half g (threads 256g..256g+255)
 // takes the items with odd (g = 1) or even (g = 0) position in that list.
 // Phase p: half 0 stages its item p/2 (p even) or computes item (p-1)/2 (p
 // odd); half 1 stages item (p-1)/2 (p odd) or computes item (p-2)/2 (p even,
 // p >= 2).  Every thread runs every phase and barrier.
-template <int NL, int NG>
+template <int NL, int NG, int M>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
          uint16_t* __restrict__ o, DdaGeo g) {
@@ -337,11 +396,11 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         if (rel >= 0) {
             const int j = rel >> 1;
             if (j < jh) {
-                const DdaItem it = dda_item(g, w + (2 * j + half) * G);
+                const int idx = w + (2 * j + half) * G;
                 if ((rel & 1) == 0)
-                    dda_stage<NL, NG>(buf, q, k, v, g, rs, heads, it, lt, qv);
+                    dda_item_run<NL, NG, M, true>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
                 else
-                    dda_compute<NL, NG>(buf, o, g, rs, heads, it, lt, qv);
+                    dda_item_run<NL, NG, M, false>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
             }
         }
         __syncthreads();
@@ -416,12 +475,19 @@ vinf_status launch_dda(const void* q, const void* k, const void* v, const void* 
     g.S = S;
     g.C = C;
     g.nstrips = S * heads;
-    g.nitems = 0;
+    g.nchunks = g.nfull = g.nitems = 0;
     g.sl2e = scale * 1.4426950408889634f;
     if (dt == VINF_BF16) {
-        const int nfb = (nq + DDA_TQ - 1) / DDA_TQ;
-        const int64_t items = (int64_t)g.nstrips * nfb;
+        // Remainder packing: r = nq % 256 leftover queries per strip go M strips
+        // to an item when they fit M slices (M = 1: one partial item per strip).
+        const int r = nq % DDA_TQ;
+        const int M = (r > 0 && r <= DdaRemR<4>) ? 4 : ((r > 0 && r <= DdaRemR<2>) ? 2 : 1);
+        const int64_t nchunks = M == 1 ? (nq + DDA_TQ - 1) / DDA_TQ : nq / DDA_TQ;
+        const int64_t nfull = (int64_t)g.nstrips * nchunks;
+        const int64_t items = nfull + (M == 1 ? 0 : ((int64_t)g.nstrips + M - 1) / M);
         if (items > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "dual_domain_attn: too many work items");
+        g.nchunks = (int)nchunks;
+        g.nfull = (int)nfull;
         g.nitems = (int)items;
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
@@ -431,12 +497,23 @@ vinf_status launch_dda(const void* q, const void* k, const void* v, const void* 
         const uint16_t *qb = static_cast<const uint16_t*>(q), *kb = static_cast<const uint16_t*>(k),
                        *vb = static_cast<const uint16_t*>(v);
         uint16_t* ob = static_cast<uint16_t*>(o);
+        auto run = [&](auto nl, auto ng) {
+            constexpr int NL = decltype(nl)::value, NG = decltype(ng)::value;
+            if (M == 4)
+                hipLaunchKernelGGL((dda_bf16<NL, NG, 4>), grid, block, 0, st, qb, kb, vb, ob, g);
+            else if (M == 2)
+                hipLaunchKernelGGL((dda_bf16<NL, NG, 2>), grid, block, 0, st, qb, kb, vb, ob, g);
+            else
+                hipLaunchKernelGGL((dda_bf16<NL, NG, 1>), grid, block, 0, st, qb, kb, vb, ob, g);
+        };
+        using K16 = std::integral_constant<int, DDA_L>;
+        using K0 = std::integral_constant<int, 0>;
         if (n_local > 0 && n_global > 0)
-            hipLaunchKernelGGL((dda_bf16<DDA_L, DDA_G>), grid, block, 0, st, qb, kb, vb, ob, g);
+            run(K16{}, K16{});
         else if (n_local > 0)
-            hipLaunchKernelGGL((dda_bf16<DDA_L, 0>), grid, block, 0, st, qb, kb, vb, ob, g);
+            run(K16{}, K0{});
         else
-            hipLaunchKernelGGL((dda_bf16<0, DDA_G>), grid, block, 0, st, qb, kb, vb, ob, g);
+            run(K0{}, K16{});
     } else {
         const int64_t nqs = (int64_t)nq * S * heads;
         const int64_t blocks = (nqs + 63) / 64;
