@@ -91,7 +91,86 @@ def cpu_baseline(F, C, G, side=16):
     return {"value": vox / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
             "sample": f"oracle chain (GroupNorm stats+apply, conv3, attention) in fp64 on F={F}, "
                       f"{H}x{W} locations, C={C}: {vox} voxels in {dt:.2f} s",
-            "seconds": dt}
+            "seconds": dt, "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def percentiles(samples):
+    """p10 / p50 / p90 (ms) of a list of per-step times."""
+    import numpy as np
+
+    a = np.asarray(samples, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.percentile(a, 50)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def config3_calls(vinf, steps, stream):
+    """Each call, and the step, at the per-level shape F=1024, 32x20 locations,
+    C=640 (10 heads), bf16, 32 groups: timed alone, HIP events on the launch
+    stream, seeded N(0,1) inputs."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    F, H, W, C, G, cfg = 1024, 32, 20, 640, 32, 3
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = up(synth.make_tensor(cfg, synth.X_GN, F, H, W, C, synth.BF16))
+    wt = up(synth.make_conv_weight(cfg, C, synth.BF16))
+    q = up(synth.make_tensor(cfg, synth.Q, F, H, W, C, synth.BF16))
+    k = up(synth.make_tensor(cfg, synth.K, F, H, W, C, synth.BF16))
+    v = up(synth.make_tensor(cfg, synth.V, F, H, W, C, synth.BF16))
+    y, o = torch.empty_like(x), torch.empty_like(x)
+    mean = torch.empty(G, device=dev)
+    rstd = torch.empty(G, device=dev)
+    ws = torch.empty(vinf.groupnorm_workspace_bytes(F, H, W, C, G, x.dtype), device=dev, dtype=torch.uint8)
+    cws = torch.empty(vinf.temporal_conv3_gn_workspace_bytes(C, x.dtype), device=dev, dtype=torch.uint8)
+    work = algorithmic_work(F, H, W, C)
+    out = {"shape": f"F={F}, {H}x{W}, C={C}, bf16, groups={G}"}
+    calls = [
+        ("groupnorm", "hbm", lambda: vinf.groupnorm_global(x, G, out=y, mean_out=mean, rstd_out=rstd, workspace=ws,
+                                                           stream=stream)),
+        ("groupnorm_stats", "hbm", lambda: vinf.groupnorm_stats(x, G, mean_out=mean, rstd_out=rstd, workspace=ws,
+                                                                stream=stream)),
+        ("conv3_bf16", "mfma", lambda: vinf.temporal_conv3(x, wt, out=y, stream=stream)),
+        ("conv3_gn_bf16", "mfma", lambda: vinf.temporal_conv3_gn(x, wt, mean, rstd, out=y, workspace=cws,
+                                                                 stream=stream)),
+        ("dda_bf16", "hbm", lambda: vinf.dual_domain_attn(q, k, v, out=o, stream=stream)),
+    ]
+    for name, bound, fn in calls:
+        ms = timed(fn, steps, stream)
+        wk = work["conv3_bf16" if name == "conv3_gn_bf16" else name]
+        if bound == "hbm":
+            gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+            out[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        else:
+            tfl = wk["flops"] / (ms * 1e-3) / 1e12
+            out[name] = {"ms": round(ms, 4), "TFLOP/s": round(tfl, 1),
+                         "frac_mfma_bf16": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    def step():
+        vinf.groupnorm_stats(x, G, mean_out=mean, rstd_out=rstd, workspace=ws, stream=stream)
+        vinf.temporal_conv3_gn(x, wt, mean, rstd, out=y, workspace=cws, stream=stream)
+        vinf.dual_domain_attn(y, y, y, out=o, stream=stream)
+
+    ms = timed(step, steps, stream)
+    out["step"] = {"ms": round(ms, 4), "voxels_per_s": F * H * W / (ms * 1e-3),
+                   "chain": "groupnorm_stats -> temporal_conv3_gn -> dual_domain_attn (Q = K = V)"}
+    return out
 
 
 def timed(fn, steps, stream):
@@ -189,6 +268,8 @@ def main():
                     help="skip the clip-form and ablation measurements")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the chain with the normalised tensor written out")
+    ap.add_argument("--no-config3", action="store_true",
+                    help="skip the per-call timings at F=1024, 32x20, C=640")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} requested)",
@@ -252,8 +333,10 @@ def main():
             evs[i][-1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        mod_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, (name, _) in enumerate(mods)}
-        return evs[0][0].elapsed_time(evs[-1][-1]) / args.steps, mod_ms, wall
+        per = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, (name, _) in enumerate(mods)}
+        per["step"] = [e[0].elapsed_time(e[-1]) for e in evs]
+        mod_ms = {name: sum(per[name]) / args.steps for name, _ in mods}
+        return evs[0][0].elapsed_time(evs[-1][-1]) / args.steps, mod_ms, wall, {k: percentiles(v) for k, v in per.items()}
 
     work = algorithmic_work(F, H, W, C)
 
@@ -270,11 +353,11 @@ def main():
 
     unfused_chain = None
     if not args.no_unfused:
-        ms_u, mod_u, _ = run_chain(unfused)
+        ms_u, mod_u, _, _ = run_chain(unfused)
         unfused_chain = {"ms_per_step": round(ms_u, 4), "voxels_per_s": F * H * W / (ms_u * 1e-3),
                          "kernels": kernel_table(mod_u),
                          "chain": "groupnorm (stats + apply, normalised tensor written) -> conv3 -> dual_domain_attn"}
-    ms_step, mod_ms, wall = run_chain(fused)
+    ms_step, mod_ms, wall, pct = run_chain(fused)
     vox = F * H * W
     kernels = kernel_table(mod_ms)
     # dominant single-kernel module (the GroupNorm statistics are four launches)
@@ -313,6 +396,7 @@ def main():
         del kd, vd
 
     nxt = None if args.no_next else next_rows(vinf, x, cv, G, stream, args.steps)
+    c3 = None if args.no_config3 else config3_calls(vinf, args.steps, stream)
     for _, f in fused:  # o = the step's output again, for the parity check
         f()
     torch.cuda.synchronize()
@@ -350,7 +434,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "percentiles_ms": pct,
         "chain_unfused": unfused_chain,
+        "config3": c3,
         "dda_bf16_distinct_qkv": distinct,
         "next_rows": nxt,
         "wall_s_timed": wall,
