@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
                                       vp, i]
         L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, i, vp, i64, vp, vp, vp, vp, vp, vp,
                                    vp, i]
+        L.oracle_broadcast_schedule.argtypes = [i, i, vp]
+        L.oracle_broadcast_schedule.restype = ctypes.c_int
         L.oracle_round_to.argtypes = [d, i]
         L.oracle_round_to.restype = d
         for fn in ("oracle_gn_stats", "oracle_groupnorm", "oracle_conv3", "oracle_dda_keys", "oracle_dda",
@@ -220,6 +222,15 @@ def chain(x, w, G, eps=1e-5, head_dim=64, n_local=16, n_global=16, scale=0.0, lo
     if intermediates:
         return out, gn, cv, mean, rstd
     return out, mean, rstd
+
+
+def broadcast_schedule(n_steps, range_):
+    """recompute[n_steps] (0/1 uint8): which diffusion steps compute their temporal attention."""
+    out = np.empty(n_steps, dtype=np.uint8)
+    rc = lib().oracle_broadcast_schedule(int(n_steps), int(range_), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_broadcast_schedule rc={rc}")
+    return out
 
 
 def round_to(v: float, dt: int) -> float:

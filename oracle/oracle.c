@@ -476,3 +476,21 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
     free(w64);
     return rc;
 }
+
+/* ---- Reuse of temporal-attention outputs across diffusion steps ------- */
+/* The attention difference between consecutive diffusion steps is large in
+ * the first and last 15% of the steps and small in the middle 70%; in that
+ * middle band one step's attention output is broadcast to the following steps
+ * of a range.  Readings: the edge is floor(15% of n_steps) steps at each end;
+ * the middle band is [edge, n_steps - edge); inside it the steps edge,
+ * edge + range, edge + 2*range, ... compute and the others reuse the latest
+ * computed output.  recompute[i] = 1 for a step that computes. */
+int oracle_broadcast_schedule(int n_steps, int range, unsigned char* recompute) {
+    if (n_steps < 1 || range < 1 || !recompute) return 1;
+    int edge = (15 * n_steps) / 100;
+    for (int i = 0; i < n_steps; ++i) {
+        int in_middle = i >= edge && i < n_steps - edge;
+        recompute[i] = (unsigned char)(in_middle ? ((i - edge) % range == 0) : 1);
+    }
+    return 0;
+}

@@ -16,6 +16,8 @@
  *     uniformly over the whole video);
  *   - oracle_chain: the three temporal modules in a row (the paragraph that
  *     lists Attention, Conv and GroupNorm as the temporal modules);
+ *   - oracle_broadcast_schedule: the output-reuse schedule of the Pyramid
+ *     Attention Broadcast page (implementation section);
  *   - oracle_gn_clip_sums / oracle_dda_clip: the clip-parallel form (the
  *     clip-parallelism paragraph: each device's temporal module maps its clip
  *     plus context from the previous clip, the next clip and a global context
@@ -102,6 +104,13 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
                  double eps, int head_dim, int n_local, int n_global, double scale, int round_gn,
                  const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
                  double* gn_exact, double* conv_exact, double* mean, double* rstd, int nthreads);
+
+/* Which diffusion steps compute their temporal attention and which reuse the
+ * latest computed output (the Pyramid Attention Broadcast page, implementation
+ * section): every step in the first and last floor(15% * n_steps) steps
+ * computes; in the middle band the first step and every range-th step after it
+ * compute.  recompute[n_steps] receives 1 / 0. */
+int oracle_broadcast_schedule(int n_steps, int range, unsigned char* recompute);
 
 /* Round a double to the nearest value representable in dt (ties to even). */
 double oracle_round_to(double v, int dt);

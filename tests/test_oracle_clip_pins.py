@@ -238,3 +238,48 @@ def test_chain_without_groupnorm_rounding_composes_the_modules():
     # the rounded reading differs from it only through the GroupNorm rounding
     out_r, gn_r, _, _, _ = oracle.chain(x, w, G, intermediates=True)
     assert not np.array_equal(gn_r, gn) and np.abs(gn_r - gn).max() <= 2.0 ** -8 * np.abs(gn).max()
+
+
+# ------------------------------------- reuse of attention outputs across steps
+
+def test_broadcast_schedule_hand_tables():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "broadcast_schedule.json")))
+    for c in g["cases"]:
+        got = oracle.broadcast_schedule(c["n_steps"], c["range"])
+        assert list(np.nonzero(got)[0]) == c["compute"], c
+
+
+def broadcast_by_walking(n, r):
+    """Independent construction from the prose: walk the steps, broadcasting a
+    computed output to the next r - 1 steps while inside the stable middle."""
+    edge = n * 15 // 100
+    out, since = [], None
+    for i in range(n):
+        if i < edge or i >= n - edge:
+            out.append(1)
+            since = None
+            continue
+        if since is None or since == r - 1:
+            out.append(1)
+            since = 0
+        else:
+            out.append(0)
+            since += 1
+    return out
+
+
+def test_broadcast_schedule_brute_force_and_counts():
+    for n in list(range(1, 60)) + [100, 250]:
+        edge = n * 15 // 100
+        for r in (1, 2, 3, 4, 5, 7, 60):
+            got = oracle.broadcast_schedule(n, r)
+            assert list(got) == broadcast_by_walking(n, r), (n, r)
+            # every edge step computes; the middle computes ceil(middle / r) times
+            assert got[:edge].all() and got[n - edge:].all()
+            assert int(got.sum()) == 2 * edge + -(-(n - 2 * edge) // r)
+    assert oracle.broadcast_schedule(30, 1).all()
+    with pytest.raises(ValueError):
+        oracle.broadcast_schedule(0, 2)
+    with pytest.raises(ValueError):
+        oracle.broadcast_schedule(10, 0)
