@@ -249,6 +249,21 @@ def next_rows(vinf, x, cv, G, stream, steps):
     ms = timed(gn_clip, steps, stream)
     out["groupnorm_clip"] = dict(hbm_entry(ms, Fc * S * 4 * C * b),
                                  shape=f"clip of {Fc} frames, {H}x{W}x{C}, groups={G} (sums, sums, apply)")
+    # Reuse of attention outputs across a 30-step sampling schedule (range 3):
+    # the attention cost per diffusion step, averaged over the schedule.
+    n_steps, rng = 30, 3
+    sched = vinf.attn_broadcast_schedule(n_steps, rng)
+    o = torch.empty_like(cv)
+
+    def thirty():
+        for i in range(n_steps):
+            vinf.dual_domain_attn_broadcast(cv, cv, cv, o, i, sched, stream=stream)
+
+    ms = timed(thirty, max(1, steps // 10), stream)
+    out["dda_bf16_broadcast"] = {"ms_per_step": round(ms / n_steps, 4), "computed_steps": int(sum(sched)),
+                                 "steps": n_steps, "range": rng,
+                                 "shape": f"F={F}, {H}x{W}x{C}, Q = K = V; every step in the first and last 15% "
+                                          f"computes, the middle band one step in {rng}"}
     return out
 
 

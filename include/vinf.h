@@ -248,6 +248,25 @@ vinf_status vinf_dual_domain_attn_clip(const void* q, const void* k, const void*
                                        int n_post, int H, int W, int C, int head_dim, int n_local,
                                        int n_global, float scale, vinf_dtype dt, vinf_stream stream);
 
+/*
+ * Reuse of temporal-attention outputs across diffusion steps (the Pyramid
+ * Attention Broadcast page, implementation section: the attention output
+ * changes markedly between consecutive steps only in the first and last 15%
+ * of a schedule; in the middle 70% one step's output is broadcast to the
+ * following steps).  Fills recompute[0 .. n_steps-1] with 1 for a step (in
+ * sampling order) that computes its attention and 0 for a step that reuses the
+ * latest computed output:
+ *
+ *   edge = floor(15 * n_steps / 100) steps at each end always compute;
+ *   in the middle band [edge, n_steps - edge) the steps edge, edge + range,
+ *   edge + 2*range, ... compute.
+ *
+ * range 1 computes every step.  Host only: a reuse step launches nothing, the
+ * caller keeps the last output (calls vinf_dual_domain_attn with the same o on
+ * computing steps only).  Errors: n_steps < 1, range < 1, recompute NULL.
+ */
+vinf_status vinf_attn_broadcast_schedule(int n_steps, int range, unsigned char* recompute);
+
 /* Static description of a status code. */
 const char* vinf_status_string(vinf_status s);
 

@@ -291,3 +291,22 @@ def conv_gn(**kw):
 ])
 def test_conv3_gn_rejects(kw, status):
     assert conv_gn(**kw) == status
+
+
+# ----------------------------------------------- attention output reuse schedule
+
+def test_broadcast_schedule_matches_the_oracle():
+    import numpy as np
+    import oracle
+    for n in list(range(1, 50)) + [128, 1000]:
+        for r in (1, 2, 3, 4, 9, 100):
+            assert vinf.attn_broadcast_schedule(n, r) == list(oracle.broadcast_schedule(n, r)), (n, r)
+    s = vinf.attn_broadcast_schedule(30, 3)
+    assert sum(s) == 16 and s[:5] == [1, 1, 1, 1, 1] and s[5:7] == [0, 0]
+
+
+@pytest.mark.parametrize("n,r", [(0, 2), (-1, 2), (10, 0), (10, -3)])
+def test_broadcast_schedule_rejects(n, r):
+    buf = ctypes.create_string_buffer(16)
+    assert vinf.load().vinf_attn_broadcast_schedule(n, r, buf) == INVALID
+    assert vinf.load().vinf_attn_broadcast_schedule(10, 2, None) == INVALID

@@ -20,6 +20,11 @@ and the clip-parallel forms (one clip of a longer video plus its context):
     dda_clip_halo(F_total, f0, Fc, n_local=16)               -> (n_pre, n_post)
     dual_domain_attn_clip(q, k, v, F_total, f0, n_pre, n_post, k_global, v_global) -> o
 
+and the reuse of attention outputs across diffusion steps:
+
+    attn_broadcast_schedule(n_steps, range)          -> list of 0/1 (1: the step computes)
+    dual_domain_attn_broadcast(q, k, v, out, step, schedule)  -> out (recomputed or kept)
+
 Tensors are CUDA (HIP) tensors, contiguous, channels-last [F, H, W, C],
 float32 or bfloat16.  There is no CPU fallback: without the built library
 every call raises.
@@ -33,7 +38,8 @@ import torch
 
 __all__ = ["groupnorm_global", "groupnorm_workspace_bytes", "temporal_conv3", "dual_domain_attn",
            "groupnorm_clip_sums", "groupnorm_clip_apply", "dda_clip_halo", "dual_domain_attn_clip", "groupnorm_stats",
-           "temporal_conv3_gn", "temporal_conv3_gn_workspace_bytes", "VinfError",
+           "temporal_conv3_gn", "temporal_conv3_gn_workspace_bytes", "attn_broadcast_schedule",
+           "dual_domain_attn_broadcast", "VinfError",
            "library_path", "load", "VINF_F32", "VINF_BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +82,8 @@ def load() -> ctypes.CDLL:
                    "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo", "vinf_dual_domain_attn_clip",
                    "vinf_groupnorm_stats", "vinf_temporal_conv3_gn"):
             getattr(L, fn).restype = ctypes.c_int
+        L.vinf_attn_broadcast_schedule.argtypes = [i, i, ctypes.c_char_p]
+        L.vinf_attn_broadcast_schedule.restype = ctypes.c_int
         L.vinf_status_string.argtypes = [i]
         L.vinf_status_string.restype = ctypes.c_char_p
         L.vinf_last_error.argtypes = []
@@ -331,3 +339,21 @@ def dual_domain_attn_clip(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, F_t
                                             _stream(q.device, stream))
     _check("vinf_dual_domain_attn_clip", st)
     return o
+
+
+def attn_broadcast_schedule(n_steps: int, range_: int) -> list[int]:
+    """1 for a diffusion step that computes its temporal attention, 0 for one that reuses the latest output."""
+    buf = ctypes.create_string_buffer(max(int(n_steps), 1))
+    st = load().vinf_attn_broadcast_schedule(int(n_steps), int(range_), buf)
+    _check("vinf_attn_broadcast_schedule", st)
+    return list(buf.raw[:n_steps])
+
+
+def dual_domain_attn_broadcast(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, step: int,
+                               schedule, **kw) -> torch.Tensor:
+    """Diffusion step `step` of a broadcast schedule: on a computing step, the
+    attention of q, k, v into `out`; on a reuse step nothing is launched and
+    `out` keeps the latest computed output."""
+    if schedule[step]:
+        dual_domain_attn(q, k, v, out=out, **kw)
+    return out

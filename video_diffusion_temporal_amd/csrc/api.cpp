@@ -393,6 +393,30 @@ vinf_status vinf_dual_domain_attn_clip(const void* q, const void* k, const void*
                       n_global, scale, dt, (hipStream_t)stream);
 }
 
+vinf_status vinf_attn_broadcast_schedule(int n_steps, int range, unsigned char* recompute) {
+    const char* fn = "vinf_attn_broadcast_schedule";
+    if (n_steps < 1 || range < 1 || !recompute)
+        return fail(VINF_ERR_INVALID_ARG, "%s: n_steps=%d range=%d recompute=%p", fn, n_steps, range,
+                    (void*)recompute);
+    if (n_steps > 21474836) return fail(VINF_ERR_INVALID_ARG, "%s: n_steps=%d too large", fn, n_steps);
+    const int edge = 15 * n_steps / 100;  // steps at each end that always compute
+    int since_compute = 0;                // middle-band steps since the last computing one
+    for (int i = 0; i < n_steps; ++i) {
+        if (i < edge || i >= n_steps - edge) {
+            recompute[i] = 1;
+            continue;
+        }
+        if (i == edge || since_compute == range - 1) {
+            recompute[i] = 1;
+            since_compute = 0;
+        } else {
+            recompute[i] = 0;
+            ++since_compute;
+        }
+    }
+    return VINF_OK;
+}
+
 const char* vinf_status_string(vinf_status s) {
     switch (s) {
         case VINF_OK: return "ok";
