@@ -28,6 +28,15 @@
 //     is the sum of the same bf16-rounded weights, so the output is an exact
 //     convex combination of the V rows up to fp32 rounding.
 //   * Output: fp32 -> bf16 (nearest even), 128-byte row per lane.
+//   * Frame ranges (DdaGeo): the queries' frames and the frames the K/V
+//     buffers hold are given separately, and the 16 global rows may come from
+//     buffers of their own, so one clip of a longer video with its
+//     neighbours' context frames runs the same code; the whole video is the
+//     case where both ranges are the video and the global rows are read in
+//     place.
+//   * Key sets: the bf16 kernel is templated on the local and global keys
+//     present (16 or 0 each): the full method, local context only, global
+//     context only.
 //   * Remainders: when the query count leaves r = nq % 256 queries per strip
 //     (a clip of 288 frames: 32), M strips share one item (M = 4 for r <= 36,
 //     2 for r <= 104), each in its own slice of the buffer with 4/M waves, so

@@ -21,7 +21,9 @@
 //   gn_apply            y = x * a_c + b_c with a_c = rstd_g*gamma_c and
 //                       b_c = beta_c - mean_g*a_c, forward again (its first
 //                       rows are the ones the second sweep read last).
-// HBM traffic: three reads and one write of the tensor.
+// HBM traffic: three reads and one write of the tensor.  Without y (the
+// statistics alone, when the conv applies the normalisation itself) the apply
+// is skipped: two reads.
 //
 // Clip form (the clip-parallelism paragraph: every device holds one clip and
 // the statistics are aggregated across devices): the same sweeps over one

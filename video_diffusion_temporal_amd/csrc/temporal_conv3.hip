@@ -10,8 +10,8 @@
 //
 // bf16 kernel (conv3_bf16): an implicit GEMM with M = F*S output voxels,
 // N = C_out, K = 3*C_in, on v_mfma_f32_16x16x32_bf16.
-//   * A tile is 16 frames x 16 locations (256 rows of M) by BN = 32*NF output
-//     channels (all of C_out when NF = 10 and C = 320).  For each 32-channel
+//   * A tile is 16 frames x 16 locations (256 rows of M) by BN = 16*NF*WN
+//     output channels (all 320 with NF = 5, WN = 4).  For each 32-channel
 //     slice of C_in, 18 frames x 16 locations of x (the 16 frames plus one
 //     halo frame per side) and the three taps' weight rows are staged in LDS;
 //     a tap is then a shift of the x operand by one frame (16 LDS rows), so
@@ -32,7 +32,7 @@
 //     before use).  The weight fragment is the MFMA's A operand, so
 //     each lane's accumulator holds 4 consecutive output channels of one
 //     voxel and the epilogue writes 8-byte pieces of channel-contiguous rows.
-//   * Persistent: one 512-thread workgroup per CU walks a contiguous range of
+//   * Persistent: one 256*WN-thread workgroup per CU walks a contiguous range of
 //     tiles (consecutive frame blocks of the same locations, so halo frames
 //     are L2 hits); LDS is double-buffered across slices and tiles with one
 //     barrier per slice, and the next slice's loads are in flight while the
@@ -45,9 +45,10 @@
 // forms them) is what the conv multiplies, but it is never written to HBM.
 // In the bf16 kernel each x slice lands in LDS raw (DMA); every wave then
 // rewrites the frame blocks its own loads filled, in place, as
-// fmaf(x, a_c, b_c) rounded to bf16, before the slice's one barrier.  Each lane's 16-byte slot
-// of a block always holds the same 8 channels of the slice, so a lane needs
-// 8 (a, b) pairs per slice, loaded while the previous slice is multiplied.
+// fmaf(x, a_c, b_c) rounded to bf16, before the slice's one barrier.  Each
+// lane's 16-byte slot of a block always holds the same 8 channels of the
+// slice, so a lane needs 8 (a, b) pairs per slice, loaded while the previous
+// slice is multiplied.
 // Zero pads stay zero (they are zeros of the normalised tensor); context
 // frames are raw neighbouring frames and are normalised like the rest.  The
 // result is bit for bit that of the GroupNorm apply followed by the conv.
