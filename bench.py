@@ -173,11 +173,12 @@ def config3_calls(vinf, steps, stream):
     return out
 
 
-def timed(fn, steps, stream):
-    """Average ms of fn() over `steps` calls (HIP events on the launch stream)."""
+def timed(fn, steps, stream, warm=2):
+    """Average ms of fn() over `steps` calls (HIP events on the launch stream),
+    after `warm` untimed calls."""
     import torch
 
-    for _ in range(2):
+    for _ in range(warm):
         fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -220,8 +221,10 @@ def next_rows(vinf, x, cv, G, stream, steps):
     kg.copy_(x[:16])
     vg.copy_(x[16:32])
     o = torch.empty_like(q)
+    # The clip call is short and follows a pause (the buffers are filled above):
+    # the clock takes some tens of launches to settle, hence the longer warm-up.
     ms = timed(lambda: vinf.dual_domain_attn_clip(q, k, v, F_total, f0, pre, post, kg, vg, out=o, stream=stream),
-               steps, stream)
+               steps, stream, warm=30)
     out["dda_bf16_clip"] = dict(hbm_entry(ms, S * C * b * (2 * Fc + 2 * n_ext + 32)),
                                 shape=f"clip [{f0},{f0 + Fc}) of {F_total} frames, context {pre}+{post}, "
                                       f"{H}x{W}x{C}, distinct q/k/v, external global rows")
