@@ -50,12 +50,15 @@ def lib() -> ctypes.CDLL:
                                       vp, i]
         L.oracle_chain.argtypes = [vp, vp, i, i64, i64, i64, i64, d, i, i, i, d, i, vp, i64, vp, vp, vp, vp, vp, vp,
                                    vp, i]
+        L.oracle_qkv_project.argtypes = [vp, vp, vp, i, i64, i64, i64, vp, i64, vp, i]
+        L.oracle_qkv_dda.argtypes = [vp, vp, vp, i, i64, i64, i64, i, i, i, d, vp, i64, vp, vp, i]
         L.oracle_broadcast_schedule.argtypes = [i, i, vp]
         L.oracle_broadcast_schedule.restype = ctypes.c_int
         L.oracle_round_to.argtypes = [d, i]
         L.oracle_round_to.restype = d
         for fn in ("oracle_gn_stats", "oracle_groupnorm", "oracle_conv3", "oracle_dda_keys", "oracle_dda",
-                   "oracle_chain", "oracle_gn_clip_sums", "oracle_dda_clip"):
+                   "oracle_chain", "oracle_gn_clip_sums", "oracle_dda_clip", "oracle_qkv_project",
+                   "oracle_qkv_dda"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -222,6 +225,41 @@ def chain(x, w, G, eps=1e-5, head_dim=64, n_local=16, n_global=16, scale=0.0, lo
     if intermediates:
         return out, gn, cv, mean, rstd
     return out, mean, rstd
+
+
+def qkv_project(x, w, bias=None, locs=None, nthreads=0):
+    """out[3, F, n_locs, C]: Q, K and V of every token; w is [3, C_out, C_in], bias [3, C] or None."""
+    x, w = _c(x), _c(w)
+    F, S, C = _fsc(x)
+    assert w.shape == (3, C, C) and w.dtype == x.dtype
+    locs = _locs(locs, S)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64).reshape(3 * C)
+    out = np.empty((3, F, locs.size, C))
+    rc = lib().oracle_qkv_project(_ptr(x), _ptr(w), _ptr(b), _dt(x), F, S, C, _ptr(locs), locs.size, _ptr(out),
+                                  nthreads)
+    if rc:
+        raise ValueError(f"oracle_qkv_project rc={rc}")
+    return out
+
+
+def qkv_dda(x, w, bias=None, head_dim=64, n_local=16, n_global=16, scale=0.0, locs=None, nthreads=0,
+            intermediates=False):
+    """Projection -> Q, K, V rounded to the I/O type -> dual-domain attention.
+
+    Returns o[F, n_locs, C]; with intermediates=True (o, qkv) where qkv
+    [3, F, n_locs, C] holds the rounded Q, K and V the attention read."""
+    x, w = _c(x), _c(w)
+    F, S, C = _fsc(x)
+    assert w.shape == (3, C, C) and w.dtype == x.dtype
+    locs = _locs(locs, S)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64).reshape(3 * C)
+    out = np.empty((F, locs.size, C))
+    qkv = np.empty((3, F, locs.size, C)) if intermediates else None
+    rc = lib().oracle_qkv_dda(_ptr(x), _ptr(w), _ptr(b), _dt(x), F, S, C, head_dim, n_local, n_global, scale,
+                              _ptr(locs), locs.size, _ptr(out), _ptr(qkv), nthreads)
+    if rc:
+        raise ValueError(f"oracle_qkv_dda rc={rc}")
+    return (out, qkv) if intermediates else out
 
 
 def broadcast_schedule(n_steps, range_):

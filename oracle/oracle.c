@@ -399,6 +399,107 @@ int oracle_dda_clip(const void* q, const void* k, const void* v, const void* k_g
     return dda_run(&c, nthreads);
 }
 
+/* ---- Query, key and value tokens ------------------------------------- */
+/* The attention takes the query token from frame t and computes the key and
+ * value tokens from the tokens of its frame set.  The plain reading is the
+ * usual attention layer's three linear maps of each token, with no mixing of
+ * frames or locations: out[p][f][s][co] = bias[p][co] + sum_ci
+ * w[p][co][ci] * x[f][s][ci], p = 0, 1, 2 for Q, K, V. */
+
+typedef struct {
+    const void *x, *w;
+    const double* bias;
+    int dt;
+    int64_t F, S, C, n_locs;
+    const int64_t* locs;
+    double* out;
+} proj_ctx;
+
+static void proj_locs(void* vctx, int64_t l0, int64_t l1, int tid) {
+    (void)tid;
+    proj_ctx* c = (proj_ctx*)vctx;
+    int64_t F = c->F, S = c->S, C = c->C, nl = c->n_locs;
+    double* tok = (double*)malloc(sizeof(double) * (size_t)C);
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(3 * C * C));
+    if (!tok || !wd) abort();
+    for (int64_t i = 0; i < 3 * C * C; ++i) wd[i] = load(c->w, c->dt, i);
+    for (int64_t li = l0; li < l1; ++li) {
+        int64_t s = c->locs[li];
+        for (int64_t f = 0; f < F; ++f) {
+            for (int64_t ci = 0; ci < C; ++ci) tok[ci] = load(c->x, c->dt, (f * S + s) * C + ci);
+            for (int64_t p = 0; p < 3; ++p)
+                for (int64_t co = 0; co < C; ++co) {
+                    const double* wr = wd + (p * C + co) * C;
+                    double acc = c->bias ? c->bias[p * C + co] : 0.0;
+                    for (int64_t ci = 0; ci < C; ++ci) acc += wr[ci] * tok[ci];
+                    c->out[((p * F + f) * nl + li) * C + co] = acc;
+                }
+        }
+    }
+    free(tok);
+    free(wd);
+}
+
+int oracle_qkv_project(const void* x, const void* w, const double* bias, int dt, int64_t F, int64_t S, int64_t C,
+                       const int64_t* locs, int64_t n_locs, double* out, int nthreads) {
+    if (!x || !w || !out || !locs || dt < 0 || dt > 2 || F < 1 || S < 1 || C < 1 || n_locs < 0) return 1;
+    for (int64_t i = 0; i < n_locs; ++i)
+        if (locs[i] < 0 || locs[i] >= S) return 1;
+    nthreads = resolve_threads(nthreads);
+    if (nthreads > n_locs) nthreads = n_locs > 0 ? (int)n_locs : 1;
+    proj_ctx c = {x, w, bias, dt, F, S, C, n_locs, locs, out};
+    parallel_ranges(n_locs, nthreads, proj_locs, &c);
+    return 0;
+}
+
+/* Store the rounded values v[0..n) in dt (exact: each is a dt value). */
+static void store_rounded(double* v, size_t n, int dt, void* t) {
+    for (size_t i = 0; i < n; ++i) {
+        v[i] = oracle_round_to(v[i], dt);
+        if (dt == 0) {
+            ((float*)t)[i] = (float)v[i];
+        } else {
+            float f = (float)v[i];
+            uint32_t u;
+            memcpy(&u, &f, 4);
+            ((uint16_t*)t)[i] = (uint16_t)(u >> 16);
+        }
+    }
+}
+
+/* Projection, then the attention over the projected tokens.  Q, K and V are
+ * tensors of the I/O type, so each is rounded to dt before the attention
+ * reads it.  The location subset stays exact (neither step mixes spatial
+ * locations). */
+int oracle_qkv_dda(const void* x, const void* w, const double* bias, int dt, int64_t F, int64_t S, int64_t C,
+                   int head_dim, int n_local, int n_global, double scale, const int64_t* locs, int64_t n_locs,
+                   double* out, double* qkv_out, int nthreads) {
+    if (!out || n_locs < 1 || (dt != 0 && dt != 1)) return 1;
+    size_t n = (size_t)(F * n_locs * C);
+    double* pr = (double*)malloc(sizeof(double) * 3 * n);
+    char* t = (char*)malloc((dt == 0 ? 4 : 2) * 3 * n);
+    int64_t* seq = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_locs);
+    if (!pr || !t || !seq) {
+        free(pr);
+        free(t);
+        free(seq);
+        return 2;
+    }
+    int rc = oracle_qkv_project(x, w, bias, dt, F, S, C, locs, n_locs, pr, nthreads);
+    if (rc == 0) {
+        const size_t tb = (dt == 0 ? 4 : 2) * n;
+        for (int p = 0; p < 3; ++p) store_rounded(pr + p * n, n, dt, t + p * tb);
+        if (qkv_out) memcpy(qkv_out, pr, sizeof(double) * 3 * n);
+        for (int64_t i = 0; i < n_locs; ++i) seq[i] = i;
+        rc = oracle_dda(t, t + tb, t + 2 * tb, dt, F, n_locs, C, head_dim, n_local, n_global, scale, seq, n_locs,
+                        out, nthreads);
+    }
+    free(pr);
+    free(t);
+    free(seq);
+    return rc;
+}
+
 /* ---- The three modules in a row --------------------------------------- */
 /* Each module's output is a tensor of the I/O type, so intermediates are
  * rounded to dt before they feed the next module.  With round_gn == 0 the

@@ -16,6 +16,9 @@
  *     uniformly over the whole video);
  *   - oracle_chain: the three temporal modules in a row (the paragraph that
  *     lists Attention, Conv and GroupNorm as the temporal modules);
+ *   - oracle_qkv_project / oracle_qkv_dda: the query, key and value tokens the
+ *     dual-domain attention paragraph computes from the layer's tokens (a
+ *     linear map each), and the attention over them;
  *   - oracle_broadcast_schedule: the output-reuse schedule of the Pyramid
  *     Attention Broadcast page (implementation section);
  *   - oracle_gn_clip_sums / oracle_dda_clip: the clip-parallel form (the
@@ -104,6 +107,21 @@ int oracle_chain(const void* x, const void* w, int dt, int64_t F, int64_t S, int
                  double eps, int head_dim, int n_local, int n_global, double scale, int round_gn,
                  const int64_t* locs, int64_t n_locs, double* out, double* gn_out, double* conv_out,
                  double* gn_exact, double* conv_exact, double* mean, double* rstd, int nthreads);
+
+/* Q, K and V tokens (the dual-domain attention paragraph: the query token of
+ * frame t, keys and values computed from the tokens of its frame set):
+ * out[p][f][s][co] = bias[p][co] + sum_ci w[p][co][ci] * x[f][s][ci] for
+ * p = 0, 1, 2 (Q, K, V).  w is [3][C][C] in dt, bias [3][C] double or NULL;
+ * out is [3][F][n_locs][C]. */
+int oracle_qkv_project(const void* x, const void* w, const double* bias, int dt, int64_t F, int64_t S, int64_t C,
+                       const int64_t* locs, int64_t n_locs, double* out, int nthreads);
+
+/* oracle_qkv_project -> round Q, K and V to dt -> dual-domain attention.
+ * qkv_out ([3][F][n_locs][C], the rounded values the attention reads) may be
+ * NULL.  dt 0 or 1 only. */
+int oracle_qkv_dda(const void* x, const void* w, const double* bias, int dt, int64_t F, int64_t S, int64_t C,
+                   int head_dim, int n_local, int n_global, double scale, const int64_t* locs, int64_t n_locs,
+                   double* out, double* qkv_out, int nthreads);
 
 /* Which diffusion steps compute their temporal attention and which reuse the
  * latest computed output (the Pyramid Attention Broadcast page, implementation
