@@ -202,8 +202,12 @@ def next_rows(vinf, x, cv, G, stream, steps):
     288 frames) at the same 64x40x320 bf16 locations, with its 8 + 7 context
     frames and the 16 gathered global rows, as one device of an 8-way clip
     split would run it.  Ablations: the local-only and global-only key sets at
-    F=1024 on the chain's conv output (Q = K = V)."""
+    F=1024 on the chain's conv output (Q = K = V).  Projection: Q, K and V as
+    three C x C maps of the conv output's tokens, and the attention over them."""
+    import numpy as np
     import torch
+
+    import synth
 
     F, H, W, C = x.shape
     S, b = H * W, 2
@@ -252,6 +256,22 @@ def next_rows(vinf, x, cv, G, stream, steps):
     ms = timed(gn_clip, steps, stream)
     out["groupnorm_clip"] = dict(hbm_entry(ms, Fc * S * 4 * C * b),
                                  shape=f"clip of {Fc} frames, {H}x{W}x{C}, groups={G} (sums, sums, apply)")
+    # Q/K/V projection of the chain's conv output (weights of variance 1/C),
+    # then the attention over the three projected tensors.
+    wq_np = synth.make_qkv_weight(SEED_CONFIG, C, synth.BF16)
+    wq = torch.from_numpy(wq_np.view(np.int16)).view(torch.bfloat16).to(x.device)
+    qkv = tuple(torch.empty_like(cv) for _ in range(3))
+    ms = timed(lambda: vinf.qkv_project(cv, wq, out=qkv, stream=stream), steps, stream)
+    pflops, pbytes = 6 * C * C * F * S, F * S * 4 * C * b
+    out["qkv_project_bf16"] = {"ms": round(ms, 4), "TFLOP/s": round(pflops / (ms * 1e-3) / 1e12, 1),
+                               "frac_mfma_bf16": round(pflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               **hbm_entry(ms, pbytes),
+                               "shape": f"F={F}, {H}x{W}x{C}: q, k, v = three {C}x{C} maps of every token"}
+    o = torch.empty_like(cv)
+    ms = timed(lambda: vinf.projected_dual_domain_attn(cv, wq, out=o, qkv=qkv, stream=stream), steps, stream)
+    out["projected_dda_bf16"] = {"ms": round(ms, 4), "voxels_per_s": F * S / (ms * 1e-3),
+                                 "shape": f"F={F}, {H}x{W}x{C}: qkv_project, then dual_domain_attn on q, k, v"}
+    del qkv, o
     # Reuse of attention outputs across a 30-step sampling schedule (range 3):
     # the attention cost per diffusion step, averaged over the schedule.
     n_steps, rng = 30, 3

@@ -178,6 +178,27 @@ vinf_status vinf_dual_domain_attn(const void* q, const void* k, const void* v, v
                                   vinf_dtype dt, vinf_stream stream);
 
 /*
+ * Query, key and value tokens of the attention (dual-domain attention
+ * paragraph: the query token comes from frame t, and the keys and values are
+ * computed from the tokens of its frame set).  Each is a linear map of every
+ * token, with no mixing of frames or locations:
+ *
+ *   q[f,h,w,co] = bias[0][co] + sum_ci weight[0][co][ci] * x[f,h,w,ci]
+ *   k: weight[1], bias[1];  v: weight[2], bias[2]
+ *
+ * x, q, k, v  [F][H][W][C] in dt; q, k and v must not overlap x, weight,
+ *           bias or each other.
+ * weight    [3][C_out=C][C_in=C] in dt (a torch Linear weight is [C_out][C_in]).
+ * bias      [3][C] float32 or NULL.
+ * Limits    bf16: C % 32 == 0 (bf16 MFMA tiles); f32: C % 4 == 0.
+ * bf16 runs on the matrix cores (the conv's kernel with one tap and the three
+ * maps as three output tiles), fp32 accumulate, rounded to bf16 once.  The
+ * attention over the result is vinf_dual_domain_attn(q, k, v, ...).
+ */
+vinf_status vinf_qkv_project(const void* x, const void* weight, const float* bias, void* q, void* k, void* v,
+                             int F, int H, int W, int C, vinf_dtype dt, vinf_stream stream);
+
+/*
  * GroupNorm of one clip with statistics over the whole video (the clip-
  * parallelism paragraph: each device holds a clip and its temporal modules
  * exchange context; for GroupNorm the context is the aggregated statistics

@@ -70,11 +70,12 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def seed_for(config: int, tensor_id: int) -> int:
-    """Seed of tensor ``tensor_id`` (Q=0, K=1, V=2, X_gn=3, X_conv=4, W=5, ctx_pre=6, ctx_post=7)."""
+    """Seed of tensor ``tensor_id`` (Q=0, K=1, V=2, X_gn=3, X_conv=4, W=5, ctx_pre=6, ctx_post=7,
+    W_qkv=8)."""
     return 0x5EED0000 + 16 * config + tensor_id
 
 
-Q, K, V, X_GN, X_CONV, W, CTX_PRE, CTX_POST = range(8)
+Q, K, V, X_GN, X_CONV, W, CTX_PRE, CTX_POST, W_QKV = range(9)
 
 # Workloads.  Shapes are those of VideoCrafter2 latents at 512x320 (64x40 at
 # the top level, 32x20x640 and 16x10x1280 further down), frame counts 16, 128,
@@ -101,6 +102,13 @@ def make_tensor(config: int, tensor_id: int, F: int, H: int, W: int, C: int, dty
 def make_conv_weight(config: int, C: int, dtype: int, nthreads: int = 0) -> np.ndarray:
     """[3][C_out][C_in] weights with variance 1/(3C)."""
     return normal(3 * C * C, seed_for(config, W), dtype, (1.0 / (3.0 * C)) ** 0.5, 0, 0.0,
+                  nthreads).reshape(3, C, C)
+
+
+def make_qkv_weight(config: int, C: int, dtype: int, nthreads: int = 0) -> np.ndarray:
+    """[3][C_out][C_in] Q/K/V projection weights with variance 1/C (a token of
+    unit variance maps to unit variance)."""
+    return normal(3 * C * C, seed_for(config, W_QKV), dtype, (1.0 / C) ** 0.5, 0, 0.0,
                   nthreads).reshape(3, C, C)
 
 

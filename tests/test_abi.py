@@ -36,7 +36,7 @@ def test_exports_every_declared_function():
     assert set(names) >= {"vinf_groupnorm_global", "vinf_temporal_conv3", "vinf_dual_domain_attn",
                           "vinf_groupnorm_workspace_bytes", "vinf_status_string", "vinf_last_error",
                           "vinf_groupnorm_clip_sums", "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo",
-                          "vinf_dual_domain_attn_clip"}
+                          "vinf_dual_domain_attn_clip", "vinf_qkv_project"}
     lib = ctypes.CDLL(vinf.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -106,6 +106,29 @@ def test_conv_rejects(kw, status):
     assert conv(**kw) == status
 
 
+def proj(**kw):
+    a = dict(x=A, w=B, bias=None, q=Cp, k=D, v=E, F=16, H=8, W=5, C=64, dt=BF16)
+    a.update(kw)
+    return vinf.load().vinf_qkv_project(a["x"], a["w"], a["bias"], a["q"], a["k"], a["v"], a["F"], a["H"], a["W"],
+                                        a["C"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(q=None), INVALID), (dict(k=None), INVALID),
+    (dict(v=None), INVALID),
+    (dict(x=A + 4), INVALID), (dict(q=Cp + 8), INVALID), (dict(v=E + 2), INVALID), (dict(bias=Fp + 2), INVALID),
+    (dict(F=0), INVALID), (dict(H=0), INVALID), (dict(C=-32), INVALID), (dict(dt=5), INVALID),
+    (dict(C=48), UNSUPPORTED),                    # bf16 needs C % 32 == 0
+    (dict(C=6, dt=F32), UNSUPPORTED),             # f32 needs C % 4 == 0
+    (dict(q=A), INVALID), (dict(k=A + 16 * 40 * 64 * 2 - 16), INVALID),   # an output overlaps x
+    (dict(v=B + 64), INVALID), (dict(bias=Fp, k=Fp + 128), INVALID),    # an output overlaps weight / bias
+    (dict(k=Cp), INVALID), (dict(v=Cp + 256), INVALID), (dict(v=D + 512), INVALID),   # outputs overlap
+])
+def test_qkv_project_rejects(kw, status):
+    assert proj(**kw) == status
+    assert vinf.load().vinf_last_error()
+
+
 def gn(**kw):
     L = vinf.load()
     a = dict(x=A, y=B, gamma=None, beta=None, mean=None, rstd=None, F=16, H=8, W=5, C=64, G=8, eps=1e-5, dt=F32,
@@ -141,6 +164,8 @@ def test_python_binding_requires_gpu_tensors():
         vinf.temporal_conv3(x, torch.zeros(3, 64, 64))
     with pytest.raises(TypeError):
         vinf.groupnorm_global(x, 8)
+    with pytest.raises(TypeError):
+        vinf.qkv_project(x, torch.zeros(3, 64, 64))
 
 
 # ------------------------------------------------------------ clip forms

@@ -82,6 +82,7 @@ def load() -> ctypes.CDLL:
                    "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo", "vinf_dual_domain_attn_clip",
                    "vinf_groupnorm_stats", "vinf_temporal_conv3_gn"):
             getattr(L, fn).restype = ctypes.c_int
+        L.vinf_qkv_project.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
         L.vinf_attn_broadcast_schedule.argtypes = [i, i, ctypes.c_char_p]
         L.vinf_attn_broadcast_schedule.restype = ctypes.c_int
         L.vinf_status_string.argtypes = [i]
@@ -192,6 +193,42 @@ def dual_domain_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
                                        float(scale), _dtype_code(q), _stream(q.device, stream))
     _check("vinf_dual_domain_attn", st)
     return o
+
+
+def qkv_project(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                out: tuple[torch.Tensor, torch.Tensor, torch.Tensor] | None = None,
+                stream=None) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(q, k, v): the three C x C maps of weight [3, C_out, C_in] (bias [3, C]
+    float32 or None) applied to every token of x [F, H, W, C]."""
+    _dev(x, "x")
+    _dev(weight, "weight")
+    F, H, W, C = _fhwc(x)
+    if tuple(weight.shape) != (3, C, C) or weight.dtype != x.dtype:
+        raise ValueError(f"weight must be [3,{C},{C}] of {x.dtype}")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != 3 * C):
+        raise ValueError("bias must be float32 [3, C]")
+    if out is None:
+        out = tuple(torch.empty_like(x) for _ in range(3))
+    q, k, v = (_dev(t, n) for t, n in zip(out, "qkv"))
+    for t in (q, k, v):
+        if t.shape != x.shape or t.dtype != x.dtype:
+            raise ValueError("q, k and v must have the shape and dtype of x")
+    st = load().vinf_qkv_project(_ptr(x), _ptr(weight), _ptr(bias), _ptr(q), _ptr(k), _ptr(v), F, H, W, C,
+                                 _dtype_code(x), _stream(x.device, stream))
+    _check("vinf_qkv_project", st)
+    return q, k, v
+
+
+def projected_dual_domain_attn(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                               out: torch.Tensor | None = None, qkv: tuple | None = None, head_dim: int = 64,
+                               n_local: int = 16, n_global: int = 16, scale: float = 0.0,
+                               stream=None) -> torch.Tensor:
+    """Dual-domain attention over the projected tokens of x: vinf_qkv_project
+    then vinf_dual_domain_attn on one stream.  qkv: optional (q, k, v) buffers
+    shaped like x."""
+    q, k, v = qkv_project(x, weight, bias, out=qkv, stream=stream)
+    return dual_domain_attn(q, k, v, out=out, head_dim=head_dim, n_local=n_local, n_global=n_global, scale=scale,
+                            stream=stream)
 
 
 def _workspace(x: torch.Tensor, groups: int, workspace):

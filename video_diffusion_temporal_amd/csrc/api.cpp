@@ -255,6 +255,32 @@ vinf_status vinf_temporal_conv3(const void* x, const void* ctx_pre, const void* 
     return launch_conv3(x, ctx_pre, ctx_post, weight, bias, y, F, H * W, C, dt, (hipStream_t)stream);
 }
 
+vinf_status vinf_qkv_project(const void* x, const void* weight, const float* bias, void* q, void* k, void* v,
+                             int F, int H, int W, int C, vinf_dtype dt, vinf_stream stream) {
+    const char* fn = "vinf_qkv_project";
+    size_t bytes;
+    VINF_TRY(check_shape(fn, F, H, W, C, dt, &bytes));
+    VINF_TRY(check_tensor(fn, "x", x, true));
+    VINF_TRY(check_tensor(fn, "weight", weight, true));
+    VINF_TRY(check_tensor(fn, "q", q, true));
+    VINF_TRY(check_tensor(fn, "k", k, true));
+    VINF_TRY(check_tensor(fn, "v", v, true));
+    VINF_TRY(check_f32(fn, "bias", bias));
+    if (dt == VINF_BF16 && C % 32)
+        return fail(VINF_ERR_UNSUPPORTED, "%s: bf16 needs C %% 32 == 0 (MFMA tiles), got C=%d", fn, C);
+    const size_t wbytes = (size_t)3 * C * C * dtype_bytes(dt);
+    const void* outs[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+        const void* o = outs[i];
+        if (overlap(o, bytes, x, bytes) || overlap(o, bytes, weight, wbytes) || overlap(o, bytes, bias, (size_t)3 * C * 4))
+            return fail(VINF_ERR_INVALID_ARG, "%s: %c overlaps an input", fn, "qkv"[i]);
+        for (int j = 0; j < i; ++j)
+            if (overlap(o, bytes, outs[j], bytes))
+                return fail(VINF_ERR_INVALID_ARG, "%s: %c overlaps %c", fn, "qkv"[i], "qkv"[j]);
+    }
+    return launch_qkv_project(x, weight, bias, q, k, v, F, H * W, C, dt, (hipStream_t)stream);
+}
+
 size_t vinf_temporal_conv3_gn_workspace_bytes(int C, vinf_dtype dt) {
     if (C < 1 || (dt != VINF_F32 && dt != VINF_BF16)) return 0;
     return conv3_gn_workspace(C, dt);

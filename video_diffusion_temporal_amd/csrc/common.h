@@ -89,6 +89,10 @@ vinf_status launch_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_
                             const float* bias, const float* mean, const float* rstd, const float* gamma,
                             const float* beta, int groups, void* y, int F, int S, int C, vinf_dtype dt,
                             void* workspace, hipStream_t stream);
+// Q, K and V = the three C x C maps of w ([3][C][C]) applied to every token of
+// x (bf16: the conv's MFMA kernel with one tap; fp32: one element per thread).
+vinf_status launch_qkv_project(const void* x, const void* w, const float* bias, void* q, void* k, void* v, int F,
+                               int S, int C, vinf_dtype dt, hipStream_t st);
 
 // Attention of query frames f0 .. f0+nq-1 of an F-frame video; k/v hold
 // frames kf0 .. kend-1; kg/vg the global rows or null (read from k/v).

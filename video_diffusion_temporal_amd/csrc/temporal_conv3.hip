@@ -8,6 +8,12 @@
 //
 //   y[f,s,co] = bias[co] + sum_k sum_ci W[k][co][ci] * xt[f+k-1, s, ci]
 //
+// The same kernel with one tap is the Q/K/V projection (dual-domain attention
+// paragraph: the query token is frame t's, and keys and values are computed
+// from the tokens of its frame set; read as three linear maps of each token):
+//
+//   q/k/v[f,s,co] = bias[p][co] + sum_ci W[p][co][ci] * x[f, s, ci],  p = 0, 1, 2
+//
 // bf16 kernel (conv3_bf16): an implicit GEMM with M = F*S output voxels,
 // N = C_out, K = 3*C_in, on v_mfma_f32_16x16x32_bf16.
 //   * A tile is 16 frames x 16 locations (256 rows of M) by BN = 16*NF*WN
@@ -37,7 +43,10 @@
 //     are L2 hits); LDS is double-buffered across slices and tiles with one
 //     barrier per slice, and the next slice's loads are in flight while the
 //     current one is multiplied.
-// fp32 kernel (conv3_f32): one output element per thread, fp32 FMA.
+// Projection (TAPS = 1): the 16 tile frames are staged with no halo and no
+// shift, N runs over the 3*C weight rows, and each tile writes to the output
+// its channels belong to; KS = 2 slices share a barrier.
+// fp32 kernels (conv3_f32, qkv_project_f32): one output element per thread, fp32 FMA.
 //
 // GroupNorm applied inside the conv (conv3_bf16<.., GN = true>, conv3_f32
 // with gn tables): the GroupNorm output g = x*a_c + b_c (a_c = rstd_g*gamma_c,
@@ -62,31 +71,47 @@ typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
 constexpr int CV_TF = 16;                       // frames per tile
 constexpr int CV_TP = 16;                       // locations per tile
-constexpr int CV_AROWS = (CV_TF + 2) * CV_TP;   // 288 staged x rows
 constexpr int CV_BK = 32;                       // C_in slice
 
-template <int NF, int WN>
+// LDS of one slice: the staged x frames (16 + TAPS - 1 of them: the tile's
+// frames plus the halo the taps reach) and TAPS weight slices of BN rows.
+// A stage (one barrier) holds KS consecutive slices; two stages alternate.
+template <int NF, int WN, int TAPS, int KS>
 struct ConvLds {
     static constexpr int BN = 16 * NF * WN;
-    static constexpr int A_BYTES = CV_AROWS * 64;
-    static constexpr int B_BYTES = 3 * BN * 64;
-    static constexpr int BUF = A_BYTES + B_BYTES;
+    static constexpr int NSTG = CV_TF + TAPS - 1;
+    static constexpr int A_BYTES = NSTG * CV_TP * 64;
+    static constexpr int B_BYTES = TAPS * BN * 64;
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int BUF = KS * SLOT;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t cv_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int NF, int WN, bool GN>
+// TAPS = 3: the temporal conv (tap k multiplies frame f+k-1, one output y).
+// TAPS = 1: the Q/K/V projection, the same GEMM with no frame shift: N spans
+// the 3*C rows of the [3][C][C] weight, and output channel n goes to
+// y, y1 or y2 (Q, K, V) by n / C.  Tiles of one location block are
+// consecutive, so a workgroup stages each x tile from L2 for the second and
+// third output.  With one tap a slice holds a third of the conv's MFMAs, so
+// KS = 2 slices share a barrier (more work in flight per load latency).
+template <int NF, int WN, int TAPS, int KS, bool GN>
 __global__ void __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(WN, WN)))
 conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, const uint16_t* __restrict__ post,
            const uint16_t* __restrict__ w, const float* __restrict__ bias, const float* __restrict__ gn_a,
-           const float* __restrict__ gn_b, uint16_t* __restrict__ y, int F, int S, int C, int nfb, int nlb,
-           int ntn) {
-    using L = ConvLds<NF, WN>;
+           const float* __restrict__ gn_b, uint16_t* y, uint16_t* y1, uint16_t* y2, int F, int S, int C, int nfb,
+           int nlb, int ntn) {
+    static_assert(TAPS == 1 || TAPS == 3, "kernel 3 or a plain projection");
+    static_assert(!GN || (TAPS == 3 && KS == 1), "GroupNorm inside only for the conv");
+    using L = ConvLds<NF, WN, TAPS, KS>;
     constexpr int BN = L::BN;
+    constexpr int NSTG = L::NSTG;               // staged frames
+    constexpr int HALO = (TAPS - 1) / 2;        // frames before the tile
+    constexpr int NA = TAPS + 3;                // x fragments per wave and slice
     constexpr int NW = 4 * WN;                  // waves: 4 along M x WN along N
-    constexpr int B_INSTR = 3 * BN / 16;        // wave instructions per weight slice (16 rows each)
+    constexpr int B_INSTR = TAPS * BN / 16;     // wave instructions per weight slice (16 rows each)
     __shared__ __attribute__((aligned(1024))) char lds[2 * L::BUF];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -115,38 +140,44 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         n0 = nt * BN;
     };
 
-    // Issue the loads of slice kc of tile t into buffer b.
-    auto issue = [&](int t, int kc, int b) {
+    // Issue the loads of slices kc .. kc+KS-1 of tile t into buffer b.
+    auto issue = [&](int t, int kc0, int b) {
         int f0, s0, n0;
         tile_coords(t, f0, s0, n0);
-        char* abuf = lds + b * L::BUF;
-        char* bbuf = abuf + L::A_BYTES;
-        const uint32_t loc_off = ((uint32_t)(s0 + st_row) * (uint32_t)C + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
-        const uint32_t voff = s0 + st_row < S ? loc_off : frame_bytes;   // past the end: zeros
-        for (int i = wv; i < CV_TF + 2; i += NW) {                      // one frame per instruction
-            const int f = f0 - 1 + i;
-            const void* base = x;
-            uint32_t nrec = 0;
-            if (f >= 0 && f < F) {
-                base = x + (int64_t)f * S * C;
-                nrec = frame_bytes;
-            } else if (f == -1 && pre) {
-                base = pre;
-                nrec = frame_bytes;
-            } else if (f == F && post) {
-                base = post;
-                nrec = frame_bytes;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kc = kc0 + ks;
+            char* abuf = lds + b * L::BUF + ks * L::SLOT;
+            char* bbuf = abuf + L::A_BYTES;
+            const uint32_t loc_off =
+                ((uint32_t)(s0 + st_row) * (uint32_t)C + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
+            const uint32_t voff = s0 + st_row < S ? loc_off : frame_bytes;   // past the end: zeros
+            for (int i = wv; i < NSTG; i += NW) {                           // one frame per instruction
+                const int f = f0 - HALO + i;
+                const void* base = x;
+                uint32_t nrec = 0;
+                if (f >= 0 && f < F) {
+                    base = x + (int64_t)f * S * C;
+                    nrec = frame_bytes;
+                } else if (f == -1 && pre) {
+                    base = pre;
+                    nrec = frame_bytes;
+                } else if (f == F && post) {
+                    base = post;
+                    nrec = frame_bytes;
+                }
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(cv_rsrc(base, nrec),
+                                                         (__attribute__((address_space(3))) void*)(abuf + i * 1024), 16,
+                                                         voff, 0, 0, 0);
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(cv_rsrc(base, nrec),
-                                                     (__attribute__((address_space(3))) void*)(abuf + i * 1024), 16,
-                                                     voff, 0, 0, 0);
-        }
-        for (int i = wv; i < B_INSTR; i += NW) {                        // 16 weight rows per instruction
-            const int r = 16 * i + st_row;                              // r = tap*BN + co
-            const int tap = r / BN, co = r - tap * BN;
-            const uint32_t off = ((uint32_t)((tap * C + n0 + co) * C) + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(bbuf + i * 1024),
-                                                     16, off, 0, 0, 0);
+            for (int i = wv; i < B_INSTR; i += NW) {                        // 16 weight rows per instruction
+                const int r = 16 * i + st_row;                              // r = tap*BN + co (tap 0 when TAPS = 1)
+                const int tap = r / BN, co = r - tap * BN;
+                const uint32_t off =
+                    ((uint32_t)((tap * C + n0 + co) * C) + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(bbuf + i * 1024),
+                                                         16, off, 0, 0, 0);
+            }
         }
     };
 
@@ -174,8 +205,8 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
     auto gn_apply_tile = [&](int t, char* abuf) {
         int f0, s0, n0;
         tile_coords(t, f0, s0, n0);
-        for (int i = wv; i < CV_TF + 2; i += NW) {
-            const int f = f0 - 1 + i;
+        for (int i = wv; i < NSTG; i += NW) {
+            const int f = f0 - HALO + i;
             if (!((f >= 0 && f < F) || (f == -1 && pre) || (f == F && post))) continue;
             u32x4_t* p = reinterpret_cast<u32x4_t*>(abuf + i * 1024 + lane * 16);
             const u32x4_t u = *p;
@@ -194,58 +225,65 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         issue(t_begin, 0, 0);
         gn_load(0);
     }
-    int g = 0;  // slice counter across tiles (selects the buffer)
+    int g = 0;  // stage counter across tiles (selects the buffer)
     for (int t = t_begin; t < t_end; ++t) {
-        for (int kc = 0; kc < nk; ++kc, ++g) {
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of slice g are in LDS
+        for (int kc = 0; kc < nk; kc += KS, ++g) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of stage g are in LDS
             // Each wave normalises the frame blocks its own loads filled (the
             // same blocks issue() gives it), so its own vmcnt wait suffices.
             if constexpr (GN) gn_apply_tile(t, lds + (g & 1) * L::BUF);
-            __syncthreads();                      // everyone's are (normalised); slice g-1 is no longer read
-            if (kc + 1 < nk)
-                issue(t, kc + 1, (g + 1) & 1);
+            __syncthreads();                      // everyone's are (normalised); stage g-1 is no longer read
+            if (kc + KS < nk)
+                issue(t, kc + KS, (g + 1) & 1);
             else if (t + 1 < t_end)
                 issue(t + 1, 0, (g + 1) & 1);
-            const char* abuf = lds + (g & 1) * L::BUF;
-            const char* bbuf = abuf + L::A_BYTES;
-            bf16x8v a[6];
 #pragma unroll
-            for (int j = 0; j < 6; ++j)
-                a[j] = *reinterpret_cast<const bf16x8v*>(abuf + (wm * 64 + j * 16) * 64 + rd_off);
-            // (tap, ni) groups of 4 MFMAs; weight fragments are read LA groups ahead.
-            constexpr int NG = 3 * NF, LA = 3;
-            auto bfrag = [&](int gidx) {
-                const int tap = gidx / NF, ni = gidx - tap * NF;
-                return *reinterpret_cast<const bf16x8v*>(bbuf + (tap * BN + wn * 16 * NF + ni * 16) * 64 + rd_off);
-            };
-            bf16x8v bq[LA];
+            for (int ks = 0; ks < KS; ++ks) {
+                const char* abuf = lds + (g & 1) * L::BUF + ks * L::SLOT;
+                const char* bbuf = abuf + L::A_BYTES;
+                bf16x8v a[NA];
 #pragma unroll
-            for (int q = 0; q < LA; ++q)
-                if (q < NG) bq[q] = bfrag(q);
+                for (int j = 0; j < NA; ++j)
+                    a[j] = *reinterpret_cast<const bf16x8v*>(abuf + (wm * 64 + j * 16) * 64 + rd_off);
+                // (tap, ni) groups of 4 MFMAs; weight fragments are read LA groups ahead.
+                constexpr int NG = TAPS * NF, LA = NG < 3 ? NG : 3;
+                auto bfrag = [&](int gidx) {
+                    const int tap = gidx / NF, ni = gidx - tap * NF;
+                    return *reinterpret_cast<const bf16x8v*>(bbuf + (tap * BN + wn * 16 * NF + ni * 16) * 64 +
+                                                             rd_off);
+                };
+                bf16x8v bq[LA];
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const int tap = gi / NF, ni = gi - tap * NF;
-                const bf16x8v b = bq[gi % LA];
-                if (gi + LA < NG) bq[gi % LA] = bfrag(gi + LA);
+                for (int q = 0; q < LA; ++q)
+                    if (q < NG) bq[q] = bfrag(q);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[mi + tap], acc[mi][ni], 0, 0, 0);
-            }
-            // Keep the fragment reads LA groups ahead of their MFMAs.
-            __builtin_amdgcn_sched_group_barrier(0x100, 6 + LA, 0);
+                for (int gi = 0; gi < NG; ++gi) {
+                    const int tap = gi / NF, ni = gi - tap * NF;
+                    const bf16x8v b = bq[gi % LA];
+                    if (gi + LA < NG) bq[gi % LA] = bfrag(gi + LA);
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-                if (gi + LA < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    for (int mi = 0; mi < 4; ++mi)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[mi + tap], acc[mi][ni], 0, 0, 0);
+                }
+                // Keep the fragment reads LA groups ahead of their MFMAs.
+                __builtin_amdgcn_sched_group_barrier(0x100, NA + LA, 0);
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                    if (gi + LA < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
             }
             // the next slice's GroupNorm coefficients, in flight over the wait at the loop top
             if constexpr (GN) gn_load(kc + 1 < nk ? kc + 1 : 0);
         }
         // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, location
-        // s0 + lane%16, channels n0 + wn*16*NF + ni*16 + 4*(lane/16) + 0..3.
+        // s0 + lane%16, channels n0 + wn*16*NF + ni*16 + 4*(lane/16) + 0..3
+        // of output n0 / C (BN divides C, so a tile stays in one output).
         int f0, s0, n0;
         tile_coords(t, f0, s0, n0);
         const int s = s0 + lr;
+        const int po = TAPS == 3 ? 0 : n0 / C;
+        uint16_t* yo = TAPS == 3 ? y : (po == 0 ? y : (po == 1 ? y1 : y2));
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int f = f0 + 4 * wm + mi;
@@ -263,7 +301,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
                     uint2 o;
                     o.x = pack_bf16x2(acc[mi][ni][0] + b0, acc[mi][ni][1] + b1);
                     o.y = pack_bf16x2(acc[mi][ni][2] + b2, acc[mi][ni][3] + b3);
-                    *reinterpret_cast<uint2*>(y + ((int64_t)f * S + s) * C + n) = o;
+                    *reinterpret_cast<uint2*>(yo + ((int64_t)f * S + s) * C + (n - po * C)) = o;
                 }
                 acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
@@ -305,6 +343,23 @@ __global__ void __launch_bounds__(256) conv3_f32(const float* __restrict__ x, co
     y[idx] = acc;
 }
 
+// float32 I/O Q/K/V projection: one output element per thread, fp32 FMA;
+// element idx of the [3][F*S][C] output space goes to q, k or v.
+__global__ void __launch_bounds__(256) qkv_project_f32(const float* __restrict__ x, const float* __restrict__ w,
+                                                       const float* __restrict__ bias, float* q, float* k, float* v,
+                                                       int64_t FS, int C) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= 3 * FS * C) return;
+    const int co = (int)(idx % C);
+    const int64_t row = (idx / C) % FS;
+    const int p = (int)(idx / (FS * C));
+    const float* xr = x + row * C;
+    const float* wr = w + ((int64_t)p * C + co) * C;
+    float acc = bias ? bias[p * C + co] : 0.f;
+    for (int ci = 0; ci < C; ++ci) acc = fmaf(wr[ci], xr[ci], acc);
+    (p == 0 ? q : (p == 1 ? k : v))[row * C + co] = acc;
+}
+
 // The GroupNorm coefficients per channel, in fp32 exactly as the GroupNorm
 // apply forms them: a_c = rstd_g * gamma_c, b_c = beta_c - mean_g * a_c.
 __global__ void __launch_bounds__(256) conv3_gn_coeffs(const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -326,10 +381,15 @@ __global__ void __launch_bounds__(256) conv3_gn_coeffs(const float* __restrict__
 namespace vinf_host {
 using namespace vinf;
 
-template <int NF, int WN>
+// TAPS = 3: the conv into y.  TAPS = 1: the projection into y, y1, y2, KS
+// slices per barrier (C / 32 must be a multiple of KS).
+template <int NF, int WN, int TAPS = 3, int KS = 1>
 static vinf_status launch_bf16(const void* x, const void* pre, const void* post, const void* w, const float* bias,
-                               const float* gn_a, const float* gn_b, void* y, int F, int S, int C, hipStream_t st) {
-    const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP, ntn = C / ConvLds<NF, WN>::BN;
+                               const float* gn_a, const float* gn_b, void* y, int F, int S, int C, hipStream_t st,
+                               void* y1 = nullptr, void* y2 = nullptr) {
+    constexpr int NOUT = TAPS == 3 ? 1 : 3;
+    const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP,
+              ntn = NOUT * C / ConvLds<NF, WN, TAPS, KS>::BN;
     const int64_t tiles = (int64_t)nfb * nlb * ntn;
     if (tiles > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: too many tiles");
     if ((uint64_t)S * C * 2 >= 0x80000000ull || (uint64_t)3 * C * C * 2 >= 0x80000000ull)
@@ -341,12 +401,17 @@ static vinf_status launch_bf16(const void* x, const void* pre, const void* post,
     const uint16_t *xb = static_cast<const uint16_t*>(x), *pb = static_cast<const uint16_t*>(pre),
                    *qb = static_cast<const uint16_t*>(post), *wb = static_cast<const uint16_t*>(w);
     uint16_t* yb = static_cast<uint16_t*>(y);
-    if (gn_a)
-        hipLaunchKernelGGL((conv3_bf16<NF, WN, true>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias, gn_a,
-                           gn_b, yb, F, S, C, nfb, nlb, ntn);
-    else
-        hipLaunchKernelGGL((conv3_bf16<NF, WN, false>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias,
-                           gn_a, gn_b, yb, F, S, C, nfb, nlb, ntn);
+    uint16_t* y1b = y1 ? static_cast<uint16_t*>(y1) : yb;
+    uint16_t* y2b = y2 ? static_cast<uint16_t*>(y2) : yb;
+    if constexpr (TAPS == 3) {
+        if (gn_a) {
+            hipLaunchKernelGGL((conv3_bf16<NF, WN, 3, 1, true>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias,
+                               gn_a, gn_b, yb, y1b, y2b, F, S, C, nfb, nlb, ntn);
+            return VINF_OK;
+        }
+    }
+    hipLaunchKernelGGL((conv3_bf16<NF, WN, TAPS, KS, false>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias,
+                       gn_a, gn_b, yb, y1b, y2b, F, S, C, nfb, nlb, ntn);
     return VINF_OK;
 }
 
@@ -403,6 +468,33 @@ vinf_status launch_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_
     const vinf_status r = run_conv3(x, ctx_pre, ctx_post, weight, bias, a, b, y, F, S, C, dt, st);
     if (r != VINF_OK) return r;
     return check_launch("temporal_conv3_gn");
+}
+
+vinf_status launch_qkv_project(const void* x, const void* w, const float* bias, void* q, void* k, void* v, int F,
+                               int S, int C, vinf_dtype dt, hipStream_t st) {
+    if (dt == VINF_BF16) {
+        vinf_status r;
+        // C / 32 is even whenever C is a multiple of 64: two slices per barrier.
+        if (C % 320 == 0)
+            r = launch_bf16<5, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+        else if (C % 256 == 0)
+            r = launch_bf16<4, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+        else if (C % 128 == 0)
+            r = launch_bf16<2, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+        else if (C % 64 == 0)
+            r = launch_bf16<2, 2, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+        else
+            r = launch_bf16<1, 2, 1, 1>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+        if (r != VINF_OK) return r;
+    } else {
+        const int64_t FS = (int64_t)F * S;
+        const int64_t blocks = (3 * FS * C + 255) / 256;
+        if (blocks > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "qkv_project: grid too large");
+        hipLaunchKernelGGL(qkv_project_f32, dim3((uint32_t)blocks), dim3(256), 0, st, static_cast<const float*>(x),
+                           static_cast<const float*>(w), bias, static_cast<float*>(q), static_cast<float*>(k),
+                           static_cast<float*>(v), FS, C);
+    }
+    return check_launch("qkv_project");
 }
 
 }  // namespace vinf_host
