@@ -38,6 +38,8 @@ def to_bf16_bits(a):
     (1, 3, 3, 64, BF, True),
     (2, 2, 2, 32, BF, True),      # the narrowest tile (32 channels)
     (3, 5, 5, 640, BF, False),    # two N tiles per output
+    (4, 2, 3, 1280, BF, True),    # four N tiles per output (twelve per launch)
+    (7, 3, 5, 96, BF, True),      # C / 32 odd: one slice per barrier
     (17, 4, 3, 96, FP, True),
     (9, 2, 5, 32, FP, False),
 ])
