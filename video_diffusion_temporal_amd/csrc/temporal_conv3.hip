@@ -37,7 +37,10 @@
 //     with scheduling-group hints; the compiler otherwise reads them just
 //     before use).  The weight fragment is the MFMA's A operand, so
 //     each lane's accumulator holds 4 consecutive output channels of one
-//     voxel and the epilogue writes 8-byte pieces of channel-contiguous rows.
+//     voxel.  The epilogue swaps fragment pairs across lane groups
+//     (v_permlane32_swap, v_permlane16_swap) so that a lane holds 8
+//     consecutive channels and writes 16-byte pieces (64 contiguous bytes of
+//     a voxel row per store instruction).
 //   * Persistent: one 256*WN-thread workgroup per CU walks a contiguous range of
 //     tiles (consecutive frame blocks of the same locations, so halo frames
 //     are L2 hits); LDS is double-buffered across slices and tiles with one
@@ -284,27 +287,38 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         const int s = s0 + lr;
         const int po = TAPS == 3 ? 0 : n0 / C;
         uint16_t* yo = TAPS == 3 ? y : (po == 0 ? y : (po == 1 ? y1 : y2));
+        // Output channels of fragment pairs (ni, ni+1) go out as 16-byte
+        // pieces: lane group g (= lane / 16) holds 4 channels of each fragment;
+        // a 32-lane swap and then a 16-lane swap leave group g with channels
+        // 8g .. 8g+7 of the pair (g = 0, 1 from fragment ni, g = 2, 3 from
+        // ni+1), so each store covers 64 contiguous bytes of a voxel row.
+        auto packed = [&](int mi, int ni, int half) {
+            const int n = n0 + wn * 16 * NF + ni * 16 + 4 * lc + 2 * half;
+            const float b0 = bias ? bias[n] : 0.f, b1 = bias ? bias[n + 1] : 0.f;
+            return pack_bf16x2(acc[mi][ni][2 * half] + b0, acc[mi][ni][2 * half + 1] + b1);
+        };
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int f = f0 + 4 * wm + mi;
+            int64_t row = ((int64_t)f * S + s) * C - po * C;
 #pragma unroll
-            for (int ni = 0; ni < NF; ++ni) {
-                const int n = n0 + wn * 16 * NF + ni * 16 + 4 * lc;
-                if (f < F && s < S) {
-                    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-                    if (bias) {
-                        b0 = bias[n];
-                        b1 = bias[n + 1];
-                        b2 = bias[n + 2];
-                        b3 = bias[n + 3];
-                    }
-                    uint2 o;
-                    o.x = pack_bf16x2(acc[mi][ni][0] + b0, acc[mi][ni][1] + b1);
-                    o.y = pack_bf16x2(acc[mi][ni][2] + b2, acc[mi][ni][3] + b3);
-                    *reinterpret_cast<uint2*>(yo + ((int64_t)f * S + s) * C + (n - po * C)) = o;
-                }
-                acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int np = 0; np + 1 < NF; np += 2) {
+                auto lo = __builtin_amdgcn_permlane32_swap(packed(mi, np, 0), packed(mi, np + 1, 0), false, false);
+                lo = __builtin_amdgcn_permlane16_swap(lo[0], lo[1], false, false);
+                auto hi = __builtin_amdgcn_permlane32_swap(packed(mi, np, 1), packed(mi, np + 1, 1), false, false);
+                hi = __builtin_amdgcn_permlane16_swap(hi[0], hi[1], false, false);
+                const int nb = n0 + wn * 16 * NF + np * 16 + 8 * lc;
+                if (f < F && s < S)
+                    *reinterpret_cast<u32x4_t*>(yo + row + nb) = u32x4_t{lo[0], hi[0], lo[1], hi[1]};
             }
+            if constexpr (NF & 1) {
+                const int ni = NF - 1;
+                const int n = n0 + wn * 16 * NF + ni * 16 + 4 * lc;
+                const uint2 o = {packed(mi, ni, 0), packed(mi, ni, 1)};
+                if (f < F && s < S) *reinterpret_cast<uint2*>(yo + row + n) = o;
+            }
+#pragma unroll
+            for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
 }
