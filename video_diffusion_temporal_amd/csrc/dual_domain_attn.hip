@@ -27,7 +27,13 @@
 //     pair rows, 64 v_dot2c each, into 64 fp32 accumulators.  The normaliser
 //     is the sum of the same bf16-rounded weights, so the output is an exact
 //     convex combination of the V rows up to fp32 rounding.
-//   * Output: fp32 -> bf16 (nearest even), 128-byte row per lane.
+//   * Output: fp32 -> bf16 (nearest even), 128-byte row per lane.  The 8
+//     lanes of a group (8 consecutive frames) transpose their 16-byte chunks
+//     through three ds_swizzle exchanges (lane distances 4, 2, 1), so each
+//     store instruction writes 8 whole 128-byte rows (8 lanes per frame)
+//     rather than 64 pieces of 16 bytes in 64 different lines.  Lanes past
+//     the last query therefore stay in the group (computing the last query
+//     again) and only skip their stores.
 //   * Frame ranges (DdaGeo): the queries' frames and the frames the K/V
 //     buffers hold are given separately, and the 16 global rows may come from
 //     buffers of their own, so one clip of a longer video with its
@@ -141,6 +147,9 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
             qv[4 * c + 2] = u[2];
             qv[4 * c + 3] = u[3];
         }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) qv[c] = 0u;  // a lane past the last query computes a throw-away copy
     }
     if constexpr (NL > 0) {
         const int tlast = min(it.t0 + R, g.f0 + g.nq) - 1;
@@ -237,8 +246,11 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     constexpr int NK = NL + NG;                 // keys
     constexpr int NLP = NL > 0 ? 9 : 0;         // local V pair rows
     constexpr int NP = NLP + (NG > 0 ? 8 : 0);  // V pair rows
-    const int t = it.t0 + lt;
-    if (t >= g.f0 + g.nq) return;
+    // Lanes past the last query stay in (the output transpose below moves
+    // data between the 8 lanes of a group) and compute the last query's
+    // windows; their own results are not stored.
+    const int tend = g.f0 + g.nq;
+    const int t = min(it.t0 + lt, tend - 1);
     const int s = it.strip / heads, h = it.strip % heads;
     const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int F = g.F;
@@ -339,14 +351,45 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
         }
     }
 
+    // ---- output: the 8 lanes of a group (8 consecutive frames) transpose
+    // their 8 x 16-byte chunks (xor-butterfly over lane distances 4, 2, 1),
+    // so that store k writes frame 8a+k's whole 128-byte head row with the 8
+    // lanes of group a: full cache lines instead of 64 scattered pieces ----
     const float inv = 1.f / den;
-    uint16_t* orow = o + (int64_t)(t - g.f0) * rs + col;
+    uint32_t ov[8][4];  // ov[c]: channels 8c .. 8c+7, bf16 pairs
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        u32x4_t wv;
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = pack_bf16x2(acc[8 * c + 2 * e] * inv, acc[8 * c + 2 * e + 1] * inv);
-        *reinterpret_cast<u32x4_t*>(orow + c * 8) = wv;
+        for (int e = 0; e < 4; ++e) ov[c][e] = pack_bf16x2(acc[8 * c + 2 * e] * inv, acc[8 * c + 2 * e + 1] * inv);
+    const int lb = lt & 7;
+    auto stage = [&](auto dist) {
+        constexpr int j = decltype(dist)::value;
+        constexpr int pattern = 0x1f | (j << 10);  // ds_swizzle bit mode: lane ^ j
+        const bool upper = (lb & j) != 0;
+#pragma unroll
+        for (int c0 = 0; c0 < 8; ++c0) {
+            if (c0 & j) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t send = upper ? ov[c0][e] : ov[c0 + j][e];
+                const uint32_t got = (uint32_t)__builtin_amdgcn_ds_swizzle((int)send, pattern);
+                if (upper)
+                    ov[c0][e] = got;
+                else
+                    ov[c0 + j][e] = got;
+            }
+        }
+    };
+    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 1>{});
+    // lane 8a+b now holds chunk b of frames 8a .. 8a+7 (slot k: frame 8a+k)
+    const int tg = it.t0 + (lt & ~7);
+#pragma unroll
+    for (int kf = 0; kf < 8; ++kf) {
+        if (tg + kf < tend)
+            *reinterpret_cast<u32x4_t*>(o + (int64_t)(tg + kf - g.f0) * rs + col + lb * 8) =
+                u32x4_t{ov[kf][0], ov[kf][1], ov[kf][2], ov[kf][3]};
     }
 }
 
