@@ -27,13 +27,13 @@
 //     pair rows, 64 v_dot2c each, into 64 fp32 accumulators.  The normaliser
 //     is the sum of the same bf16-rounded weights, so the output is an exact
 //     convex combination of the V rows up to fp32 rounding.
-//   * Output: fp32 -> bf16 (nearest even), 128-byte row per lane.  The 8
-//     lanes of a group (8 consecutive frames) transpose their 16-byte chunks
-//     through three ds_swizzle exchanges (lane distances 4, 2, 1), so each
-//     store instruction writes 8 whole 128-byte rows (8 lanes per frame)
-//     rather than 64 pieces of 16 bytes in 64 different lines.  Lanes past
-//     the last query therefore stay in the group (computing the last query
-//     again) and only skip their stores.
+//   * Output: fp32 -> bf16 (nearest even), 128-byte row per lane.  The 4
+//     lanes of a quad (4 consecutive frames) transpose each half of their
+//     eight 16-byte chunks through two ds_swizzle exchanges (lane distances
+//     2, 1), so each store instruction writes 64 contiguous bytes of 16
+//     frames rather than 16 bytes of 64.  Lanes past the last query
+//     therefore stay in the quad (computing the last query again) and only
+//     skip their stores.
 //   * Frame ranges (DdaGeo): the queries' frames and the frames the K/V
 //     buffers hold are given separately, and the 16 global rows may come from
 //     buffers of their own, so one clip of a longer video with its
@@ -351,17 +351,20 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
         }
     }
 
-    // ---- output: the 8 lanes of a group (8 consecutive frames) transpose
-    // their 8 x 16-byte chunks (xor-butterfly over lane distances 4, 2, 1),
-    // so that store k writes frame 8a+k's whole 128-byte head row with the 8
-    // lanes of group a: full cache lines instead of 64 scattered pieces ----
+    // ---- output: the 4 lanes of a quad (4 consecutive frames) transpose
+    // each half of their 8 x 16-byte chunks (xor-butterfly over lane
+    // distances 2, 1), so that a store writes 64 contiguous bytes (half a
+    // head row) of each of 16 frames instead of 16 bytes of each of 64 ----
     const float inv = 1.f / den;
     uint32_t ov[8][4];  // ov[c]: channels 8c .. 8c+7, bf16 pairs
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[c][e] = pack_bf16x2(acc[8 * c + 2 * e] * inv, acc[8 * c + 2 * e + 1] * inv);
-    const int lb = lt & 7;
+    const int lb = lt & 3;
+    // One butterfly stage over lane distance j within each quad: the lower
+    // lane takes the partner's chunk c0 into slot c0+j, the upper lane the
+    // partner's chunk c0+j into slot c0 (ds_swizzle reads the partner).
     auto stage = [&](auto dist) {
         constexpr int j = decltype(dist)::value;
         constexpr int pattern = 0x1f | (j << 10);  // ds_swizzle bit mode: lane ^ j
@@ -380,15 +383,16 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
             }
         }
     };
-    stage(std::integral_constant<int, 4>{});
     stage(std::integral_constant<int, 2>{});
     stage(std::integral_constant<int, 1>{});
-    // lane 8a+b now holds chunk b of frames 8a .. 8a+7 (slot k: frame 8a+k)
-    const int tg = it.t0 + (lt & ~7);
+    // lane 4a+b now holds chunks b and b+4 of frames 4a .. 4a+3 (slot k:
+    // frame 4a + k%4, chunk b + 4*(k/4))
+    const int tg = it.t0 + (lt & ~3);
 #pragma unroll
     for (int kf = 0; kf < 8; ++kf) {
-        if (tg + kf < tend)
-            *reinterpret_cast<u32x4_t*>(o + (int64_t)(tg + kf - g.f0) * rs + col + lb * 8) =
+        const int tf = tg + (kf & 3);
+        if (tf < tend)
+            *reinterpret_cast<u32x4_t*>(o + (int64_t)(tf - g.f0) * rs + col + (lb + 4 * (kf >> 2)) * 8) =
                 u32x4_t{ov[kf][0], ov[kf][1], ov[kf][2], ov[kf][3]};
     }
 }
