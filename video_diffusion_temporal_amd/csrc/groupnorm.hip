@@ -145,35 +145,40 @@ __device__ __forceinline__ float gn_rstd_of(double sq_sum, double n, float eps) 
 // stats = [mean_0..mean_{G-1}, rstd_0..rstd_{G-1}] (float).  With stats
 // non-null the block writes its statistic there (and to out, if non-null);
 // with dsum non-null it writes the raw fp64 sum to dsum[g].
+constexpr int GN_FIN_THREADS = 1024;
+
 template <bool SECOND>
-__global__ void __launch_bounds__(256) gn_finalize(const float* __restrict__ partial, float* __restrict__ stats,
-                                                   float* __restrict__ out, double* __restrict__ dsum, int B, int C,
-                                                   int cpg, int G, double n, float eps) {
-    __shared__ double red[256];
+__global__ void __launch_bounds__(GN_FIN_THREADS) gn_finalize(const float* __restrict__ partial,
+                                                              float* __restrict__ stats, float* __restrict__ out,
+                                                              double* __restrict__ dsum, int B, int C, int cpg, int G,
+                                                              double n, float eps) {
+    constexpr int NT = GN_FIN_THREADS;
+    __shared__ double red[NT];
     const int g = blockIdx.x;
-    const int64_t items = (int64_t)B * cpg;
+    const int items = B * cpg;  // <= GN_MAX_BLOCKS * C
     // item i = (block b = i / cpg, channel g*cpg + i % cpg); thread t owns items
-    // t, t+256, ...; eight loads in flight into eight fp64 partial sums.
+    // t, t+NT, ...; eight loads in flight into eight fp64 partial sums (the
+    // group's items are a few per thread, so the sweep is a few load rounds).
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int64_t i = threadIdx.x;
-    for (; i + 7 * 256 < items; i += 8 * 256) {
+    int i = threadIdx.x;
+    for (; i + 7 * NT < items; i += 8 * NT) {
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t it = i + u * 256, b = it / cpg;
-            v[u] = partial[b * C + g * cpg + (int)(it - b * cpg)];
+            const int it = i + u * NT, b = it / cpg;
+            v[u] = partial[(int64_t)b * C + g * cpg + (it - b * cpg)];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] += (double)v[u];
     }
-    for (int u = 0; i < items; i += 256, ++u) {
-        const int64_t b = i / cpg;
-        acc[u & 7] += (double)partial[b * C + g * cpg + (int)(i - b * cpg)];
+    for (int u = 0; i < items; i += NT, ++u) {
+        const int b = i / cpg;
+        acc[u & 7] += (double)partial[(int64_t)b * C + g * cpg + (i - b * cpg)];
     }
     double s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     red[threadIdx.x] = s;
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (int w = NT / 2; w > 0; w >>= 1) {
         if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
@@ -298,10 +303,10 @@ static vinf_status run(const void* x, void* y, const float* gamma, const float* 
     const int cpg = C / G;
     const double n = (double)rows * (double)cpg;
     sweep<BF16, false>(x, b, rows, C, cpg, st);
-    hipLaunchKernelGGL((gn_finalize<false>), dim3(G), dim3(256), 0, st, b.partial, b.stats, mean_out, nullptr,
+    hipLaunchKernelGGL((gn_finalize<false>), dim3(G), dim3(GN_FIN_THREADS), 0, st, b.partial, b.stats, mean_out, nullptr,
                        b.g.blocks, C, cpg, G, n, eps);
     sweep<BF16, true>(x, b, rows, C, cpg, st);
-    hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(256), 0, st, b.partial, b.stats, rstd_out, nullptr,
+    hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(GN_FIN_THREADS), 0, st, b.partial, b.stats, rstd_out, nullptr,
                        b.g.blocks, C, cpg, G, n, eps);
     if (y) apply<BF16>(x, y, gamma, beta, b, rows, C, cpg, G, st);
     return check_launch("groupnorm");
@@ -316,11 +321,11 @@ static vinf_status run_clip_sums(const void* x, const double* mean_sums, double*
         hipLaunchKernelGGL(gn_stats_from_sums, dim3((G + 255) / 256), dim3(256), 0, st, mean_sums, nullptr, b.stats,
                            nullptr, nullptr, G, n_total, 0.f);
         sweep<BF16, true>(x, b, rows, C, cpg, st);
-        hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(256), 0, st, b.partial, nullptr, nullptr, sums,
+        hipLaunchKernelGGL((gn_finalize<true>), dim3(G), dim3(GN_FIN_THREADS), 0, st, b.partial, nullptr, nullptr, sums,
                            b.g.blocks, C, cpg, G, n_total, 0.f);
     } else {
         sweep<BF16, false>(x, b, rows, C, cpg, st);
-        hipLaunchKernelGGL((gn_finalize<false>), dim3(G), dim3(256), 0, st, b.partial, nullptr, nullptr, sums,
+        hipLaunchKernelGGL((gn_finalize<false>), dim3(G), dim3(GN_FIN_THREADS), 0, st, b.partial, nullptr, nullptr, sums,
                            b.g.blocks, C, cpg, G, n_total, 0.f);
     }
     return check_launch("groupnorm_clip_sums");
