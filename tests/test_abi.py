@@ -80,6 +80,7 @@ def attn(**kw):
     (dict(dt=7), INVALID),
     (dict(o=A), INVALID), (dict(o=B + 256), INVALID),  # o overlaps q / k
     (dict(scale=float("nan")), INVALID),
+    (dict(F=1, H=1024, W=1 << 20, C=128), UNSUPPORTED),   # 2^31 (location, head) strips
 ])
 def test_attention_rejects(kw, status):
     assert attn(**kw) == status

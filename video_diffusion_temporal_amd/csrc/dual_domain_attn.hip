@@ -520,6 +520,8 @@ vinf_status launch_dda(const void* q, const void* k, const void* v, const void* 
                        int F, int f0, int nq, int kf0, int kend, int S, int C, int n_local, int n_global,
                        float scale, vinf_dtype dt, hipStream_t st) {
     const int heads = C / DDA_D;
+    if ((int64_t)S * heads > 0x7fffffff)
+        return fail(VINF_ERR_UNSUPPORTED, "dual_domain_attn: more than 2^31 (location, head) strips");
     DdaGeo g;
     g.kg = kg;
     g.vg = vg;
