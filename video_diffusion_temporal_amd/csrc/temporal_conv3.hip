@@ -224,8 +224,18 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         }
     };
 
+    // Stage cursor: tile ti, slice ki of the next stage to issue.
+    int ti = t_begin, ki = 0;
+    auto issue_next = [&](int buf) {
+        issue(ti, ki, buf);
+        ki += KS;
+        if (ki >= nk) {
+            ki = 0;
+            ++ti;
+        }
+    };
     if (t_begin < t_end) {
-        issue(t_begin, 0, 0);
+        issue_next(0);
         gn_load(0);
     }
     int g = 0;  // stage counter across tiles (selects the buffer)
@@ -236,10 +246,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
             // same blocks issue() gives it), so its own vmcnt wait suffices.
             if constexpr (GN) gn_apply_tile(t, lds + (g & 1) * L::BUF);
             __syncthreads();                      // everyone's are (normalised); stage g-1 is no longer read
-            if (kc + KS < nk)
-                issue(t, kc + KS, (g + 1) & 1);
-            else if (t + 1 < t_end)
-                issue(t + 1, 0, (g + 1) & 1);
+            if (ti < t_end) issue_next((g + 1) & 1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const char* abuf = lds + (g & 1) * L::BUF + ks * L::SLOT;
