@@ -55,6 +55,7 @@ def test_groupnorm_stats_equal_the_full_call(dt):
     (1, 3, 3, 64, 8, BF, False, True, False),      # one frame: both taps of it read pads
     (1, 3, 3, 64, 8, BF, True, True, True),
     (2, 2, 2, 32, 4, BF, False, False, True),
+    (48, 16, 95, 32, 8, BF, True, True, True),     # 285 tiles: workgroups walk several, with pads
     (17, 4, 3, 96, 8, FP, True, True, True),
     (9, 2, 5, 32, 4, FP, False, False, False),
 ])
@@ -98,6 +99,27 @@ def test_conv3_gn_vs_oracle(F, H, W, C, G, dt, ctx, bias, affine):
     if not ctx:  # without context frames: bit for bit the unfused pair of calls
         g, _, _ = vinf.groupnorm_global(xd, G, 1e-5, tg(gamma), tg(beta))
         assert np.array_equal(bits(y), bits(vinf.temporal_conv3(g, upload(w), bias=tg(b))))
+
+
+@pytest.mark.parametrize("C,G", [(320, 32), (256, 32), (128, 16), (64, 8), (32, 8)])
+def test_conv3_gn_many_tiles_bitwise(C, G):
+    """72 frames x 31 x 29 locations make 285 tiles (both axes ragged), more
+    than there are workgroups, so a workgroup normalises the next tile's first
+    slice while it multiplies the previous tile's last one.  Every tiling the
+    bf16 conv picks for these C must still equal GroupNorm apply + conv bit
+    for bit."""
+    F, H, W = 72, 31, 29
+    announce(f"conv3_gn many tiles F={F} H={H} W={W} C={C} G={G}")
+    x = upload(rnd((F, H, W, C), 4600 + C, BF, 2.0))
+    w = upload(rnd((3, C, C), 4700 + C, BF, (1.0 / (3 * C)) ** 0.5))
+    tg = lambda a: torch.from_numpy(a).to(dev())
+    gamma = tg(np.linspace(0.5, 1.5, C).astype(np.float32))
+    beta = tg(np.linspace(-0.25, 0.25, C).astype(np.float32))
+    b = tg(np.linspace(-0.1, 0.1, C).astype(np.float32))
+    mean, rstd = vinf.groupnorm_stats(x, G)
+    y = vinf.temporal_conv3_gn(x, w, mean, rstd, gamma, beta, None, None, b)
+    g, _, _ = vinf.groupnorm_global(x, G, 1e-5, gamma, beta)
+    assert torch.equal(y.view(torch.int16), vinf.temporal_conv3(g, w, bias=b).view(torch.int16))
 
 
 @pytest.mark.parametrize("dt", [BF, FP])

@@ -57,10 +57,16 @@
 // forms them) is what the conv multiplies, but it is never written to HBM.
 // In the bf16 kernel each x slice lands in LDS raw (DMA); every wave then
 // rewrites the frame blocks its own loads filled, in place, as
-// fmaf(x, a_c, b_c) rounded to bf16, before the slice's one barrier.  Each
-// lane's 16-byte slot of a block always holds the same 8 channels of the
-// slice, so a lane needs 8 (a, b) pairs per slice, loaded while the previous
-// slice is multiplied.
+// fmaf(x, a_c, b_c) rounded to bf16, before the barrier that publishes the
+// slice.  That rewrite is software-pipelined: slice g+1 is normalised while
+// slice g's last MFMA groups run (its loads were issued right after slice
+// g's barrier, and its buffer is not read before the next one), so the
+// vector work fills the matrix pipe's shadow instead of a window where every
+// wave waits.  A lane rewrites one 4-byte word (one channel pair) in four
+// rows of a block, so it needs one (a, b) pair per block: the coefficients
+// come as a table of channel pairs, and one wave stages a slice's 256 bytes
+// into LDS two slices ahead.  The first NSTG - NW waves own a second block,
+// which they rewrite after the MFMA groups.
 // Zero pads stay zero (they are zeros of the normalised tensor); context
 // frames are raw neighbouring frames and are normalised like the rest.  The
 // result is bit for bit that of the GroupNorm apply followed by the conv.
@@ -115,7 +121,8 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
     constexpr int NA = TAPS + 3;                // x fragments per wave and slice
     constexpr int NW = 4 * WN;                  // waves: 4 along M x WN along N
     constexpr int B_INSTR = TAPS * BN / 16;     // wave instructions per weight slice (16 rows each)
-    __shared__ __attribute__((aligned(1024))) char lds[2 * L::BUF];
+    // GN: two 256-byte coefficient slots and a 16-byte zero slot follow the buffers.
+    __shared__ __attribute__((aligned(1024))) char lds[2 * L::BUF + (GN ? 528 : 0)];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -190,37 +197,58 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 #pragma unroll
         for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // GroupNorm coefficients of the lane's 8 channels of slice kc (its LDS
-    // slot in every frame block holds chunk st_chunk of the slice).
-    f32x4_t gna[2], gnb[2];
-    auto gn_load = [&](int kc) {
+    // GroupNorm.  gn_a is a table of channel pairs, 16 bytes each (a_2p,
+    // a_2p+1, b_2p, b_2p+1), so a slice's coefficients are 256 contiguous
+    // bytes.  The last wave stages them into a coefficient slot two stages
+    // ahead (stage s uses slot s & 1), so every wave sees them after the
+    // barrier that precedes their use.  Lane (w = lane & 3, c = (lane >> 2) & 3,
+    // r = lane >> 4) normalises word w of chunk c in rows r, r+4, r+8, r+12 of a
+    // frame block: channel pair 4c + w of the slice, so it needs one pair of
+    // (a, b) per block.  Chunk c of row r sits at slot c ^ ((r >> 1) & 3).
+    char* const ab_lds = lds + 2 * L::BUF;
+    const int gq = ((lane >> 2) & 3) ^ (lane >> 5);
+    const int g_even = (lane >> 4) * 64 + (gq << 4) + (lane & 3) * 4;        // rows r and r + 8 (+512)
+    const int g_odd = (lane >> 4) * 64 + ((gq ^ 2) << 4) + (lane & 3) * 4;   // rows r + 4 (+256) and r + 12 (+768)
+    const int g_pair = (((lane >> 2) & 3) * 4 + (lane & 3)) * 16;
+    auto frame_live = [&](int f) { return (f >= 0 && f < F) || (f == -1 && pre != nullptr) || (f == F && post != nullptr); };
+    auto ab_issue = [&](int kc, int slot) {
         if constexpr (GN) {
-            const int c0 = kc * CV_BK + st_chunk * 8;
-            gna[0] = *reinterpret_cast<const f32x4_t*>(gn_a + c0);
-            gna[1] = *reinterpret_cast<const f32x4_t*>(gn_a + c0 + 4);
-            gnb[0] = *reinterpret_cast<const f32x4_t*>(gn_b + c0);
-            gnb[1] = *reinterpret_cast<const f32x4_t*>(gn_b + c0 + 4);
+            if (wv == NW - 1)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(cv_rsrc(gn_a, (uint32_t)C * 8u),
+                                                         (__attribute__((address_space(3))) void*)(ab_lds + slot * 256),
+                                                         4, (uint32_t)(kc * 256 + lane * 4), 0, 0, 0);
         }
     };
-    // Normalise, in place, the frame blocks of the landed x slice that this
-    // wave's own loads filled (the blocks issue() gives it).  Zero pads are
-    // zeros of the normalised tensor and stay as they are.
-    auto gn_apply_tile = [&](int t, char* abuf) {
+    // One frame block (blk) of a landed slice: read its raw words and the
+    // coefficients (the zero slot for a zero pad, which then stays zero) ...
+    auto gn_read = [&](const char* blk, bool live, int slot, uint32_t (&u)[4], f32x4_t& co) {
+        u[0] = *reinterpret_cast<const uint32_t*>(blk + g_even);
+        u[1] = *reinterpret_cast<const uint32_t*>(blk + g_odd + 256);
+        u[2] = *reinterpret_cast<const uint32_t*>(blk + g_even + 512);
+        u[3] = *reinterpret_cast<const uint32_t*>(blk + g_odd + 768);
+        co = *reinterpret_cast<const f32x4_t*>(live ? ab_lds + slot * 256 + g_pair : ab_lds + 512);
+    };
+    // ... and write back fmaf(x, a_c, b_c) rounded to bf16.
+    auto gn_write = [&](char* blk, const uint32_t (&u)[4], f32x4_t co) {
+        uint32_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(fmaf(bf_lo(u[j]), co[0], co[2]), fmaf(bf_hi(u[j]), co[1], co[3]));
+        *reinterpret_cast<uint32_t*>(blk + g_even) = v[0];
+        *reinterpret_cast<uint32_t*>(blk + g_odd + 256) = v[1];
+        *reinterpret_cast<uint32_t*>(blk + g_even + 512) = v[2];
+        *reinterpret_cast<uint32_t*>(blk + g_odd + 768) = v[3];
+    };
+    // All frame blocks this wave loaded for stage (t, slot) in buffer buf, from
+    // block index i0 on.
+    auto gn_blocks = [&](int t, int buf, int slot, int i0) {
         int f0, s0, n0;
         tile_coords(t, f0, s0, n0);
-        for (int i = wv; i < NSTG; i += NW) {
-            const int f = f0 - HALO + i;
-            if (!((f >= 0 && f < F) || (f == -1 && pre) || (f == F && post))) continue;
-            u32x4_t* p = reinterpret_cast<u32x4_t*>(abuf + i * 1024 + lane * 16);
-            const u32x4_t u = *p;
-            u32x4_t v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float lo = fmaf(bf_lo(u[j]), gna[j >> 1][2 * (j & 1)], gnb[j >> 1][2 * (j & 1)]);
-                const float hi = fmaf(bf_hi(u[j]), gna[j >> 1][2 * (j & 1) + 1], gnb[j >> 1][2 * (j & 1) + 1]);
-                v[j] = pack_bf16x2(lo, hi);
-            }
-            *p = v;
+        for (int i = i0; i < NSTG; i += NW) {
+            char* blk = lds + buf * L::BUF + i * 1024;
+            uint32_t u[4];
+            f32x4_t co;
+            gn_read(blk, frame_live(f0 - HALO + i), slot, u, co);
+            gn_write(blk, u, co);
         }
     };
 
@@ -236,17 +264,36 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
     };
     if (t_begin < t_end) {
         issue_next(0);
-        gn_load(0);
+        ab_issue(0, 0);    // stage 0
+        ab_issue(ki, 1);   // stage 1
+    }
+    if constexpr (GN) {
+        if (tid < 4) reinterpret_cast<uint32_t*>(ab_lds + 512)[tid] = 0u;
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        __syncthreads();                      // the coefficients of stages 0 and 1 and the zero slot
+        if (t_begin < t_end) gn_blocks(t_begin, 0, 0, wv);
     }
     int g = 0;  // stage counter across tiles (selects the buffer)
     for (int t = t_begin; t < t_end; ++t) {
         for (int kc = 0; kc < nk; kc += KS, ++g) {
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of stage g are in LDS
-            // Each wave normalises the frame blocks its own loads filled (the
-            // same blocks issue() gives it), so its own vmcnt wait suffices.
-            if constexpr (GN) gn_apply_tile(t, lds + (g & 1) * L::BUF);
-            __syncthreads();                      // everyone's are (normalised); stage g-1 is no longer read
+            // vmcnt(0): this wave's loads of stage g are in LDS (with GN, waited
+            // for, and normalised, while stage g-1 was multiplied).
+            if constexpr (!GN) __builtin_amdgcn_s_waitcnt(0x0f70);
+            __syncthreads();                      // everyone's are; stage g-1 is no longer read
+            const int t_next = ti;                // the tile of stage g+1, if there is one
             if (ti < t_end) issue_next((g + 1) & 1);
+            ab_issue(ki, g & 1);                  // GN: the coefficients of stage g+2
+            // GN: stage g+1 is normalised in the shadow of stage g's last MFMA
+            // groups.  Each wave rewrites the frame blocks its own loads filled,
+            // so its own vmcnt wait suffices; the next barrier publishes them.
+            // Past the last stage this rewrites a buffer no one reads again.
+            char* const nbuf = lds + ((g + 1) & 1) * L::BUF;
+            bool n_live = false;
+            if constexpr (GN) {
+                int f0, s0, n0;
+                tile_coords(t_next, f0, s0, n0);
+                n_live = frame_live(f0 - HALO + wv);
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const char* abuf = lds + (g & 1) * L::BUF + ks * L::SLOT;
@@ -266,6 +313,10 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 #pragma unroll
                 for (int q = 0; q < LA; ++q)
                     if (q < NG) bq[q] = bfrag(q);
+                // GN: the next stage's block is read after group GA and written after group GA + GL.
+                constexpr int GA = NG > 5 ? NG - 5 : 0, GL = NG - 1 - GA < 2 ? NG - 1 - GA : 2;
+                uint32_t gu[4];
+                f32x4_t gco;
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     const int tap = gi / NF, ni = gi - tap * NF;
@@ -274,6 +325,13 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 #pragma unroll
                     for (int mi = 0; mi < 4; ++mi)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[mi + tap], acc[mi][ni], 0, 0, 0);
+                    if constexpr (GN) {
+                        if (gi == GA) {
+                            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of stage g+1
+                            gn_read(nbuf + wv * 1024, n_live, (g + 1) & 1, gu, gco);
+                        }
+                        if (gi == GA + GL) gn_write(nbuf + wv * 1024, gu, gco);
+                    }
                 }
                 // Keep the fragment reads LA groups ahead of their MFMAs.
                 __builtin_amdgcn_sched_group_barrier(0x100, NA + LA, 0);
@@ -283,8 +341,9 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
                     if (gi + LA < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
-            // the next slice's GroupNorm coefficients, in flight over the wait at the loop top
-            if constexpr (GN) gn_load(kc + 1 < nk ? kc + 1 : 0);
+            // GN: a wave's further blocks (NSTG > NW: the first NSTG - NW waves).
+            if constexpr (GN && NSTG > NW)
+                if (wv + NW < NSTG) gn_blocks(t_next, (g + 1) & 1, (g + 1) & 1, wv + NW);
         }
         // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, location
         // s0 + lane%16, channels n0 + wn*16*NF + ni*16 + 4*(lane/16) + 0..3
@@ -383,9 +442,11 @@ __global__ void __launch_bounds__(256) qkv_project_f32(const float* __restrict__
 
 // The GroupNorm coefficients per channel, in fp32 exactly as the GroupNorm
 // apply forms them: a_c = rstd_g * gamma_c, b_c = beta_c - mean_g * a_c.
+// pairs = 0: two tables a[C], b[C] (the fp32 kernel).  pairs = 1: one table
+// of channel pairs (a_2p, a_2p+1, b_2p, b_2p+1) in a (the bf16 kernel).
 __global__ void __launch_bounds__(256) conv3_gn_coeffs(const float* __restrict__ mean, const float* __restrict__ rstd,
                                                        const float* __restrict__ gamma,
-                                                       const float* __restrict__ beta, int C, int cpg,
+                                                       const float* __restrict__ beta, int C, int cpg, int pairs,
                                                        float* __restrict__ a, float* __restrict__ b) {
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= C) return;
@@ -393,8 +454,14 @@ __global__ void __launch_bounds__(256) conv3_gn_coeffs(const float* __restrict__
     const float ga = gamma ? gamma[c] : 1.f;
     const float be = beta ? beta[c] : 0.f;
     const float ac = rstd[g] * ga;
-    a[c] = ac;
-    b[c] = be - mean[g] * ac;
+    const float bc = be - mean[g] * ac;
+    if (pairs) {
+        a[(c >> 1) * 4 + (c & 1)] = ac;
+        a[(c >> 1) * 4 + 2 + (c & 1)] = bc;
+    } else {
+        a[c] = ac;
+        b[c] = bc;
+    }
 }
 
 }  // namespace vinf
@@ -482,10 +549,12 @@ vinf_status launch_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_
                             const float* bias, const float* mean, const float* rstd, const float* gamma,
                             const float* beta, int groups, void* y, int F, int S, int C, vinf_dtype dt,
                             void* workspace, hipStream_t st) {
+    // bf16: the pair table (8*C bytes, C even) at the start of the workspace.
+    const int pairs = dt == VINF_BF16 ? 1 : 0;
     float* a = static_cast<float*>(workspace);
-    float* b = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)C * sizeof(float)));
+    float* b = pairs ? a : reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)C * sizeof(float)));
     hipLaunchKernelGGL(conv3_gn_coeffs, dim3((C + 255) / 256), dim3(256), 0, st, mean, rstd, gamma, beta, C,
-                       C / groups, a, b);
+                       C / groups, pairs, a, b);
     const vinf_status r = run_conv3(x, ctx_pre, ctx_post, weight, bias, a, b, y, F, S, C, dt, st);
     if (r != VINF_OK) return r;
     return check_launch("temporal_conv3_gn");
