@@ -101,14 +101,16 @@ def test_conv3_gn_vs_oracle(F, H, W, C, G, dt, ctx, bias, affine):
         assert np.array_equal(bits(y), bits(vinf.temporal_conv3(g, upload(w), bias=tg(b))))
 
 
-@pytest.mark.parametrize("C,G", [(320, 32), (256, 32), (128, 16), (64, 8), (32, 8)])
-def test_conv3_gn_many_tiles_bitwise(C, G):
-    """72 frames x 31 x 29 locations make 285 tiles (both axes ragged), more
-    than there are workgroups, so a workgroup normalises the next tile's first
-    slice while it multiplies the previous tile's last one.  Every tiling the
-    bf16 conv picks for these C must still equal GroupNorm apply + conv bit
-    for bit."""
-    F, H, W = 72, 31, 29
+@pytest.mark.parametrize("F,C,G", [(72, 320, 32), (72, 256, 32), (72, 128, 16), (72, 64, 8), (72, 32, 8),
+                                   (40, 640, 32), (24, 1280, 32)])
+def test_conv3_gn_many_tiles_bitwise(F, C, G):
+    """31 x 29 locations and 72 frames make 285 tiles (both axes ragged; 342
+    and 456 at C = 640 and 1280, where two and four channel tiles share each
+    staged x tile), more than there are workgroups, so a workgroup normalises
+    the next tile's first slice while it multiplies the previous tile's last
+    one.  Every tiling the bf16 conv picks for these C must still equal
+    GroupNorm apply + conv bit for bit."""
+    H, W = 31, 29
     announce(f"conv3_gn many tiles F={F} H={H} W={W} C={C} G={G}")
     x = upload(rnd((F, H, W, C), 4600 + C, BF, 2.0))
     w = upload(rnd((3, C, C), 4700 + C, BF, (1.0 / (3 * C)) ** 0.5))
