@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(GN_FIN_THREADS) gn_finalize(const float* __res
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = NT / 2; w > 0; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
     if (threadIdx.x == 0) {

@@ -109,8 +109,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t cv_rsrc(const void* base, uint
 template <int NF, int WN, int TAPS, int KS, bool GN>
 __global__ void __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(WN, WN)))
 conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, const uint16_t* __restrict__ post,
-           const uint16_t* __restrict__ w, const float* __restrict__ bias, const float* __restrict__ gn_a,
-           const float* __restrict__ gn_b, uint16_t* y, uint16_t* y1, uint16_t* y2, int F, int S, int C, int nfb,
+           const uint16_t* __restrict__ w, const float* __restrict__ bias, const float* __restrict__ gn_ab,
+           uint16_t* y, uint16_t* y1, uint16_t* y2, int F, int S, int C, int nfb,
            int nlb, int ntn) {
     static_assert(TAPS == 1 || TAPS == 3, "kernel 3 or a plain projection");
     static_assert(!GN || (TAPS == 3 && KS == 1), "GroupNorm inside only for the conv");
@@ -197,7 +197,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 #pragma unroll
         for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // GroupNorm.  gn_a is a table of channel pairs, 16 bytes each (a_2p,
+    // GroupNorm.  gn_ab is a table of channel pairs, 16 bytes each (a_2p,
     // a_2p+1, b_2p, b_2p+1), so a slice's coefficients are 256 contiguous
     // bytes.  The last wave stages them into a coefficient slot two stages
     // ahead (stage s uses slot s & 1), so every wave sees them after the
@@ -214,7 +214,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
     auto ab_issue = [&](int kc, int slot) {
         if constexpr (GN) {
             if (wv == NW - 1)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(cv_rsrc(gn_a, (uint32_t)C * 8u),
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(cv_rsrc(gn_ab, (uint32_t)C * 8u),
                                                          (__attribute__((address_space(3))) void*)(ab_lds + slot * 256),
                                                          4, (uint32_t)(kc * 256 + lane * 4), 0, 0, 0);
         }
@@ -473,7 +473,7 @@ using namespace vinf;
 // slices per barrier (C / 32 must be a multiple of KS).
 template <int NF, int WN, int TAPS = 3, int KS = 1>
 static vinf_status launch_bf16(const void* x, const void* pre, const void* post, const void* w, const float* bias,
-                               const float* gn_a, const float* gn_b, void* y, int F, int S, int C, hipStream_t st,
+                               const float* gn_ab, void* y, int F, int S, int C, hipStream_t st,
                                void* y1 = nullptr, void* y2 = nullptr) {
     constexpr int NOUT = TAPS == 3 ? 1 : 3;
     const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP,
@@ -492,33 +492,34 @@ static vinf_status launch_bf16(const void* x, const void* pre, const void* post,
     uint16_t* y1b = y1 ? static_cast<uint16_t*>(y1) : yb;
     uint16_t* y2b = y2 ? static_cast<uint16_t*>(y2) : yb;
     if constexpr (TAPS == 3) {
-        if (gn_a) {
+        if (gn_ab) {
             hipLaunchKernelGGL((conv3_bf16<NF, WN, 3, 1, true>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias,
-                               gn_a, gn_b, yb, y1b, y2b, F, S, C, nfb, nlb, ntn);
+                               gn_ab, yb, y1b, y2b, F, S, C, nfb, nlb, ntn);
             return VINF_OK;
         }
     }
     hipLaunchKernelGGL((conv3_bf16<NF, WN, TAPS, KS, false>), dim3(grid), dim3(256 * WN), 0, st, xb, pb, qb, wb, bias,
-                       gn_a, gn_b, yb, y1b, y2b, F, S, C, nfb, nlb, ntn);
+                       gn_ab, yb, y1b, y2b, F, S, C, nfb, nlb, ntn);
     return VINF_OK;
 }
 
-// The conv, with the GroupNorm coefficient tables gn_a / gn_b or without (null).
+// The conv, with the GroupNorm coefficients or without (null): bf16 reads the
+// channel-pair table in gn_a, fp32 the two tables gn_a / gn_b.
 static vinf_status run_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
                              const float* bias, const float* gn_a, const float* gn_b, void* y, int F, int S, int C,
                              vinf_dtype dt, hipStream_t st) {
     if (dt == VINF_BF16) {
         vinf_status r;
         if (C % 320 == 0)
-            r = launch_bf16<5, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
+            r = launch_bf16<5, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
         else if (C % 256 == 0)
-            r = launch_bf16<4, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
+            r = launch_bf16<4, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
         else if (C % 128 == 0)
-            r = launch_bf16<2, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
+            r = launch_bf16<2, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
         else if (C % 64 == 0)
-            r = launch_bf16<2, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
+            r = launch_bf16<2, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
         else
-            r = launch_bf16<1, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, gn_b, y, F, S, C, st);
+            r = launch_bf16<1, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
         if (r != VINF_OK) return r;
     } else {
         const int64_t n = (int64_t)F * S * C;
@@ -566,15 +567,15 @@ vinf_status launch_qkv_project(const void* x, const void* w, const float* bias, 
         vinf_status r;
         // C / 32 is even whenever C is a multiple of 64: two slices per barrier.
         if (C % 320 == 0)
-            r = launch_bf16<5, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+            r = launch_bf16<5, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, q, F, S, C, st, k, v);
         else if (C % 256 == 0)
-            r = launch_bf16<4, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+            r = launch_bf16<4, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, q, F, S, C, st, k, v);
         else if (C % 128 == 0)
-            r = launch_bf16<2, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+            r = launch_bf16<2, 4, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, q, F, S, C, st, k, v);
         else if (C % 64 == 0)
-            r = launch_bf16<2, 2, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+            r = launch_bf16<2, 2, 1, 2>(x, nullptr, nullptr, w, bias, nullptr, q, F, S, C, st, k, v);
         else
-            r = launch_bf16<1, 2, 1, 1>(x, nullptr, nullptr, w, bias, nullptr, nullptr, q, F, S, C, st, k, v);
+            r = launch_bf16<1, 2, 1, 1>(x, nullptr, nullptr, w, bias, nullptr, q, F, S, C, st, k, v);
         if (r != VINF_OK) return r;
     } else {
         const int64_t FS = (int64_t)F * S;
