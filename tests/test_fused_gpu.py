@@ -56,6 +56,7 @@ def test_groupnorm_stats_equal_the_full_call(dt):
     (1, 3, 3, 64, 8, BF, True, True, True),
     (2, 2, 2, 32, 4, BF, False, False, True),
     (48, 16, 95, 32, 8, BF, True, True, True),     # 285 tiles: workgroups walk several, with pads
+    (70, 16, 59, 32, 8, BF, True, False, True),    # 295 tiles, ragged last frame block, with pads
     (17, 4, 3, 96, 8, FP, True, True, True),
     (9, 2, 5, 32, 4, FP, False, False, False),
 ])
