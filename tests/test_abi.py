@@ -299,7 +299,7 @@ def conv_gn(**kw):
              F=16, H=8, W=5, C=64, dt=BF16, ws=E, wsb=None)
     a.update(kw)
     if a["wsb"] is None:
-        a["wsb"] = L.vinf_temporal_conv3_gn_workspace_bytes(64, BF16)
+        a["wsb"] = L.vinf_temporal_conv3_gn_workspace_bytes(a["C"], BF16)
     return L.vinf_temporal_conv3_gn(a["x"], a["pre"], a["post"], a["w"], a["bias"], a["mean"], a["rstd"],
                                     a["gamma"], a["beta"], a["G"], a["y"], a["F"], a["H"], a["W"], a["C"], a["dt"],
                                     a["ws"], a["wsb"], None)
@@ -314,6 +314,7 @@ def conv_gn(**kw):
     (dict(y=A), INVALID), (dict(y=B + 64), INVALID),   # y overlaps x / the weights
     (dict(ws=B), INVALID), (dict(ws=Cp + 256), INVALID),   # workspace overlaps the weights / y
     (dict(mean=Cp + 64), INVALID),                 # statistics inside y
+    (dict(F=1, H=2048, W=1639, C=320, G=32), UNSUPPORTED),   # one frame over 2 GiB (rejected before any launch)
 ])
 def test_conv3_gn_rejects(kw, status):
     assert conv_gn(**kw) == status

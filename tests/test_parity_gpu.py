@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 import video_diffusion_temporal_amd as vinf
-from helpers import announce, bits, check, check_stats, fetch, sample_locs, upload
+from helpers import announce, bits, check, check_end_to_end, check_stats, fetch, sample_locs, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -263,7 +263,11 @@ def run_chain(cfgno):
     intermediates at the bar; (3) that each GPU intermediate is the rounding
     of a value within a stated fp32 error bound of the exact one; (4) the
     final output at the bar against the oracle's attention over that
-    validated intermediate."""
+    validated intermediate; (5) the final output end to end against the
+    oracle chain: mean-abs at the bar, max-abs at the bar where both sides
+    rounded every conv value the attention reads alike, and elsewhere the
+    bar plus the bound on how far those one-step differences move the
+    attention (helpers.check_end_to_end)."""
     c = CFG[cfgno]
     F, H, W, C, G, dt = c["F"], c["H"], c["W"], c["C"], c["G"], c["dtype"]
     S = H * W
@@ -314,9 +318,12 @@ def run_chain(cfgno):
 
     # (4) final output over the validated intermediate
     cb = to_bf16_bits(cs)
-    check(os_, oracle.dda(cb, cb, cb), dt, "chain attention")
-    err = np.abs(os_ - out)
-    announce(f"  (against the oracle's own rounding choice: max-abs {err.max():.3e} mean-abs {err.mean():.3e})")
+    o_on_gpu_conv = oracle.dda(cb, cb, cb)
+    check(os_, o_on_gpu_conv, dt, "chain attention")
+
+    # (5) end to end against the oracle chain itself
+    check_end_to_end(os_, out, o_on_gpu_conv, cv_r, cs, dt, "chain")
+
 
 
 @pytest.mark.parametrize("cfgno", [1, 2, 3, 4])

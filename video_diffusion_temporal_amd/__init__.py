@@ -130,6 +130,50 @@ def _fhwc(x: torch.Tensor):
     return tuple(int(s) for s in x.shape)
 
 
+def _same_device(t: torch.Tensor, x: torch.Tensor, name: str) -> None:
+    if t.device != x.device:
+        raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+
+
+def _out_like(out: torch.Tensor | None, x: torch.Tensor, name: str = "out") -> torch.Tensor:
+    """A caller-supplied output tensor must be exactly x's shape, dtype and
+    device and contiguous: the library only sees its pointer and writes x's
+    size through it."""
+    if out is None:
+        return torch.empty_like(x)
+    _dev(out, name)
+    _same_device(out, x, name)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError(f"{name} must be {tuple(x.shape)} of {x.dtype}, got {tuple(out.shape)} of {out.dtype}")
+    return out
+
+
+def _vec(t: torch.Tensor | None, x: torch.Tensor, name: str, n: int,
+         dtype: torch.dtype = torch.float32) -> torch.Tensor | None:
+    """An optional per-channel or per-group vector: n contiguous values of dtype
+    on x's device (the library reads or writes exactly n values)."""
+    if t is None:
+        return None
+    _dev(t, name)
+    _same_device(t, x, name)
+    if t.dtype != dtype or t.numel() != n:
+        raise ValueError(f"{name} must hold {n} values of {dtype}, got {t.numel()} of {t.dtype}")
+    return t
+
+
+def _vec_out(t: torch.Tensor | None, x: torch.Tensor, name: str, n: int) -> torch.Tensor:
+    if t is None:
+        return torch.empty(n, device=x.device, dtype=torch.float32)
+    return _vec(t, x, name, n)
+
+
+def _ws(workspace: torch.Tensor, x: torch.Tensor) -> int:
+    """Bytes of a caller-supplied workspace on x's device."""
+    _dev(workspace, "workspace")
+    _same_device(workspace, x, "workspace")
+    return workspace.numel() * workspace.element_size()
+
+
 def groupnorm_workspace_bytes(F: int, H: int, W: int, C: int, groups: int, dtype: torch.dtype) -> int:
     code = VINF_BF16 if dtype == torch.bfloat16 else VINF_F32
     return int(load().vinf_groupnorm_workspace_bytes(F, H, W, C, groups, code))
@@ -142,18 +186,31 @@ def groupnorm_global(x: torch.Tensor, groups: int, eps: float = 1e-5, gamma: tor
     """GroupNorm with whole-video statistics.  Returns (y, mean[groups], rstd[groups])."""
     _dev(x, "x")
     F, H, W, C = _fhwc(x)
-    y = torch.empty_like(x) if out is None else _dev(out, "out")
-    mean = torch.empty(groups, device=x.device, dtype=torch.float32) if mean_out is None else mean_out
-    rstd = torch.empty(groups, device=x.device, dtype=torch.float32) if rstd_out is None else rstd_out
+    groups = int(groups)
+    y = _out_like(out, x)
+    mean = _vec_out(mean_out, x, "mean_out", groups)
+    rstd = _vec_out(rstd_out, x, "rstd_out", groups)
+    _vec(gamma, x, "gamma", C)
+    _vec(beta, x, "beta", C)
     need = groupnorm_workspace_bytes(F, H, W, C, groups, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _ws(workspace, x)
     st = load().vinf_groupnorm_global(_ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(mean), _ptr(rstd), F, H, W, C,
                                        groups, float(eps), _dtype_code(x), _ptr(workspace), ws_bytes,
                                        _stream(x.device, stream))
     _check("vinf_groupnorm_global", st)
     return y, mean, rstd
+
+
+def _ctx(ctx_pre, ctx_post, x: torch.Tensor) -> None:
+    F, H, W, C = _fhwc(x)
+    for name, c in (("ctx_pre", ctx_pre), ("ctx_post", ctx_post)):
+        if c is not None:
+            _dev(c, name)
+            _same_device(c, x, name)
+            if c.numel() != H * W * C or c.dtype != x.dtype:
+                raise ValueError(f"{name} must hold [H,W,C] = {H * W * C} values of {x.dtype}")
 
 
 def temporal_conv3(x: torch.Tensor, weight: torch.Tensor, ctx_pre: torch.Tensor | None = None,
@@ -165,14 +222,10 @@ def temporal_conv3(x: torch.Tensor, weight: torch.Tensor, ctx_pre: torch.Tensor 
     F, H, W, C = _fhwc(x)
     if tuple(weight.shape) != (3, C, C) or weight.dtype != x.dtype:
         raise ValueError(f"weight must be [3,{C},{C}] of {x.dtype}")
-    for name, c in (("ctx_pre", ctx_pre), ("ctx_post", ctx_post)):
-        if c is not None:
-            _dev(c, name)
-            if c.numel() != H * W * C or c.dtype != x.dtype:
-                raise ValueError(f"{name} must hold [H,W,C] = {H * W * C} values of {x.dtype}")
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != C):
-        raise ValueError("bias must be float32 [C]")
-    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    _same_device(weight, x, "weight")
+    _ctx(ctx_pre, ctx_post, x)
+    _vec(bias, x, "bias", C)
+    y = _out_like(out, x)
     st = load().vinf_temporal_conv3(_ptr(x), _ptr(ctx_pre), _ptr(ctx_post), _ptr(weight), _ptr(bias), _ptr(y), F, H,
                                      W, C, _dtype_code(x), _stream(x.device, stream))
     _check("vinf_temporal_conv3", st)
@@ -185,10 +238,11 @@ def dual_domain_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
     """Dual-domain temporal attention over [F,H,W,C] q/k/v (already projected)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev(t, name)
+        _same_device(t, q, name)
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError("q, k and v must share shape and dtype")
     F, H, W, C = _fhwc(q)
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    o = _out_like(out, q)
     st = load().vinf_dual_domain_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), F, H, W, C, head_dim, n_local, n_global,
                                        float(scale), _dtype_code(q), _stream(q.device, stream))
     _check("vinf_dual_domain_attn", st)
@@ -205,14 +259,13 @@ def qkv_project(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None
     F, H, W, C = _fhwc(x)
     if tuple(weight.shape) != (3, C, C) or weight.dtype != x.dtype:
         raise ValueError(f"weight must be [3,{C},{C}] of {x.dtype}")
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != 3 * C):
-        raise ValueError("bias must be float32 [3, C]")
+    _same_device(weight, x, "weight")
+    _vec(bias, x, "bias", 3 * C)
     if out is None:
         out = tuple(torch.empty_like(x) for _ in range(3))
-    q, k, v = (_dev(t, n) for t, n in zip(out, "qkv"))
-    for t in (q, k, v):
-        if t.shape != x.shape or t.dtype != x.dtype:
-            raise ValueError("q, k and v must have the shape and dtype of x")
+    if len(out) != 3:
+        raise ValueError("out must be a (q, k, v) triple")
+    q, k, v = (_out_like(t, x, n) for t, n in zip(out, "qkv"))
     st = load().vinf_qkv_project(_ptr(x), _ptr(weight), _ptr(bias), _ptr(q), _ptr(k), _ptr(v), F, H, W, C,
                                  _dtype_code(x), _stream(x.device, stream))
     _check("vinf_qkv_project", st)
@@ -236,13 +289,15 @@ def _workspace(x: torch.Tensor, groups: int, workspace):
     need = groupnorm_workspace_bytes(F, H, W, C, groups, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
-    return workspace, workspace.numel() * workspace.element_size()
+    return workspace, _ws(workspace, x)
 
 
-def _f64(t: torch.Tensor | None, name: str, groups: int):
+def _f64(t: torch.Tensor | None, name: str, groups: int, x: torch.Tensor | None = None):
     if t is None:
         return None
     _dev(t, name)
+    if x is not None:
+        _same_device(t, x, name)
     if t.dtype != torch.float64 or t.numel() != groups:
         raise ValueError(f"{name} must be float64 [{groups}]")
     return t
@@ -256,8 +311,9 @@ def groupnorm_clip_sums(x: torch.Tensor, groups: int, F_total: int, mean_sums: t
     clips added together and N_g counts the whole video's F_total frames."""
     _dev(x, "x")
     F, H, W, C = _fhwc(x)
-    _f64(mean_sums, "mean_sums", groups)
-    sums = torch.empty(groups, device=x.device, dtype=torch.float64) if out is None else _f64(out, "out", groups)
+    groups = int(groups)
+    _f64(mean_sums, "mean_sums", groups, x)
+    sums = torch.empty(groups, device=x.device, dtype=torch.float64) if out is None else _f64(out, "out", groups, x)
     workspace, ws_bytes = _workspace(x, groups, workspace)
     st = load().vinf_groupnorm_clip_sums(_ptr(x), _ptr(mean_sums), _ptr(sums), F, H, W, C, groups, int(F_total),
                                           _dtype_code(x), _ptr(workspace), ws_bytes, _stream(x.device, stream))
@@ -274,11 +330,16 @@ def groupnorm_clip_apply(x: torch.Tensor, groups: int, F_total: int, sums: torch
     with stats_only=True only the statistics are computed (y is None)."""
     _dev(x, "x")
     F, H, W, C = _fhwc(x)
-    _f64(sums, "sums", groups)
-    _f64(sq_sums, "sq_sums", groups)
-    y = None if stats_only else (torch.empty_like(x) if out is None else _dev(out, "out"))
-    mean = torch.empty(groups, device=x.device, dtype=torch.float32) if mean_out is None else mean_out
-    rstd = torch.empty(groups, device=x.device, dtype=torch.float32) if rstd_out is None else rstd_out
+    groups = int(groups)
+    if sums is None or sq_sums is None:
+        raise ValueError("sums and sq_sums are required")
+    _f64(sums, "sums", groups, x)
+    _f64(sq_sums, "sq_sums", groups, x)
+    y = None if stats_only else _out_like(out, x)
+    mean = _vec_out(mean_out, x, "mean_out", groups)
+    rstd = _vec_out(rstd_out, x, "rstd_out", groups)
+    _vec(gamma, x, "gamma", C)
+    _vec(beta, x, "beta", C)
     workspace, ws_bytes = _workspace(x, groups, workspace)
     st = load().vinf_groupnorm_clip_apply(None if stats_only else _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta),
                                            _ptr(sums), _ptr(sq_sums), _ptr(mean), _ptr(rstd), F, H, W, C, groups,
@@ -293,8 +354,9 @@ def groupnorm_stats(x: torch.Tensor, groups: int, eps: float = 1e-5, mean_out: t
     """Whole-video GroupNorm statistics only (the two sweeps).  Returns (mean[groups], rstd[groups])."""
     _dev(x, "x")
     F, H, W, C = _fhwc(x)
-    mean = torch.empty(groups, device=x.device, dtype=torch.float32) if mean_out is None else mean_out
-    rstd = torch.empty(groups, device=x.device, dtype=torch.float32) if rstd_out is None else rstd_out
+    groups = int(groups)
+    mean = _vec_out(mean_out, x, "mean_out", groups)
+    rstd = _vec_out(rstd_out, x, "rstd_out", groups)
     workspace, ws_bytes = _workspace(x, groups, workspace)
     st = load().vinf_groupnorm_stats(_ptr(x), _ptr(mean), _ptr(rstd), F, H, W, C, groups, float(eps), _dtype_code(x),
                                      _ptr(workspace), ws_bytes, _stream(x.device, stream))
@@ -318,23 +380,23 @@ def temporal_conv3_gn(x: torch.Tensor, weight: torch.Tensor, mean: torch.Tensor,
     F, H, W, C = _fhwc(x)
     if tuple(weight.shape) != (3, C, C) or weight.dtype != x.dtype:
         raise ValueError(f"weight must be [3,{C},{C}] of {x.dtype}")
-    for name, c in (("ctx_pre", ctx_pre), ("ctx_post", ctx_post)):
-        if c is not None:
-            _dev(c, name)
-            if c.numel() != H * W * C or c.dtype != x.dtype:
-                raise ValueError(f"{name} must hold [H,W,C] = {H * W * C} values of {x.dtype}")
+    _same_device(weight, x, "weight")
+    _ctx(ctx_pre, ctx_post, x)
     for name, v in (("mean", mean), ("rstd", rstd)):
         _dev(v, name)
         if v.dtype != torch.float32 or v.dim() != 1:
             raise ValueError(f"{name} must be float32 [groups]")
     groups = int(mean.numel())
-    if rstd.numel() != groups:
-        raise ValueError("mean and rstd must have the same length")
-    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    _vec(rstd, x, "rstd", groups)
+    _vec(mean, x, "mean", groups)
+    _vec(gamma, x, "gamma", C)
+    _vec(beta, x, "beta", C)
+    _vec(bias, x, "bias", C)
+    y = _out_like(out, x)
     need = temporal_conv3_gn_workspace_bytes(C, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _ws(workspace, x)
     st = load().vinf_temporal_conv3_gn(_ptr(x), _ptr(ctx_pre), _ptr(ctx_post), _ptr(weight), _ptr(bias), _ptr(mean),
                                        _ptr(rstd), _ptr(gamma), _ptr(beta), groups, _ptr(y), F, H, W, C,
                                        _dtype_code(x), _ptr(workspace), ws_bytes, _stream(x.device, stream))
@@ -362,14 +424,16 @@ def dual_domain_attn_clip(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, F_t
     Fc, H, W, C = _fhwc(q)
     for name, t in (("k", k), ("v", v)):
         _dev(t, name)
+        _same_device(t, q, name)
         if tuple(t.shape) != (n_pre + Fc + n_post, H, W, C) or t.dtype != q.dtype:
             raise ValueError(f"{name} must be [{n_pre + Fc + n_post},{H},{W},{C}] of {q.dtype}")
     for name, t in (("k_global", k_global), ("v_global", v_global)):
         if t is not None:
             _dev(t, name)
+            _same_device(t, q, name)
             if tuple(t.shape) != (n_global, H, W, C) or t.dtype != q.dtype:
                 raise ValueError(f"{name} must be [{n_global},{H},{W},{C}] of {q.dtype}")
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    o = _out_like(out, q)
     st = load().vinf_dual_domain_attn_clip(_ptr(q), _ptr(k), _ptr(v), _ptr(k_global), _ptr(v_global), _ptr(o),
                                             int(F_total), int(f0), Fc, int(n_pre), int(n_post), H, W, C, head_dim,
                                             n_local, n_global, float(scale), _dtype_code(q),

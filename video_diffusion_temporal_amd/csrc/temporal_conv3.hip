@@ -474,7 +474,7 @@ using namespace vinf;
 template <int NF, int WN, int TAPS = 3, int KS = 1>
 static vinf_status launch_bf16(const void* x, const void* pre, const void* post, const void* w, const float* bias,
                                const float* gn_ab, void* y, int F, int S, int C, hipStream_t st,
-                               void* y1 = nullptr, void* y2 = nullptr) {
+                               void* y1 = nullptr, void* y2 = nullptr, bool check_only = false) {
     constexpr int NOUT = TAPS == 3 ? 1 : 3;
     const int nfb = (F + CV_TF - 1) / CV_TF, nlb = (S + CV_TP - 1) / CV_TP,
               ntn = NOUT * C / ConvLds<NF, WN, TAPS, KS>::BN;
@@ -485,6 +485,7 @@ static vinf_status launch_bf16(const void* x, const void* pre, const void* post,
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return fail(VINF_ERR_HIP, "temporal_conv3: cannot query the device");
+    if (check_only) return VINF_OK;
     const int grid = (int)std::min<int64_t>(cus, tiles);
     const uint16_t *xb = static_cast<const uint16_t*>(x), *pb = static_cast<const uint16_t*>(pre),
                    *qb = static_cast<const uint16_t*>(post), *wb = static_cast<const uint16_t*>(w);
@@ -504,27 +505,29 @@ static vinf_status launch_bf16(const void* x, const void* pre, const void* post,
 }
 
 // The conv, with the GroupNorm coefficients or without (null): bf16 reads the
-// channel-pair table in gn_a, fp32 the two tables gn_a / gn_b.
+// channel-pair table in gn_a, fp32 the two tables gn_a / gn_b.  check_only:
+// run the host-side size checks and launch nothing.
 static vinf_status run_conv3(const void* x, const void* ctx_pre, const void* ctx_post, const void* weight,
                              const float* bias, const float* gn_a, const float* gn_b, void* y, int F, int S, int C,
-                             vinf_dtype dt, hipStream_t st) {
+                             vinf_dtype dt, hipStream_t st, bool check_only = false) {
     if (dt == VINF_BF16) {
         vinf_status r;
         if (C % 320 == 0)
-            r = launch_bf16<5, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
+            r = launch_bf16<5, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st, nullptr, nullptr, check_only);
         else if (C % 256 == 0)
-            r = launch_bf16<4, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
+            r = launch_bf16<4, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st, nullptr, nullptr, check_only);
         else if (C % 128 == 0)
-            r = launch_bf16<2, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
+            r = launch_bf16<2, 4>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st, nullptr, nullptr, check_only);
         else if (C % 64 == 0)
-            r = launch_bf16<2, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
+            r = launch_bf16<2, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st, nullptr, nullptr, check_only);
         else
-            r = launch_bf16<1, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st);
+            r = launch_bf16<1, 2>(x, ctx_pre, ctx_post, weight, bias, gn_a, y, F, S, C, st, nullptr, nullptr, check_only);
         if (r != VINF_OK) return r;
     } else {
         const int64_t n = (int64_t)F * S * C;
         const int64_t blocks = (n + 255) / 256;
         if (blocks > 0x7fffffff) return fail(VINF_ERR_UNSUPPORTED, "temporal_conv3: grid too large");
+        if (check_only) return VINF_OK;
         hipLaunchKernelGGL(conv3_f32, dim3((uint32_t)blocks), dim3(256), 0, st, static_cast<const float*>(x),
                            static_cast<const float*>(ctx_pre), static_cast<const float*>(ctx_post),
                            static_cast<const float*>(weight), bias, gn_a, gn_b, static_cast<float*>(y), F, S, C);
@@ -554,6 +557,10 @@ vinf_status launch_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_
     const int pairs = dt == VINF_BF16 ? 1 : 0;
     float* a = static_cast<float*>(workspace);
     float* b = pairs ? a : reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)C * sizeof(float)));
+    // Every size check runs before the coefficient kernel writes the
+    // workspace, so a rejected call leaves device memory untouched.
+    const vinf_status chk = run_conv3(x, ctx_pre, ctx_post, weight, bias, a, b, y, F, S, C, dt, st, true);
+    if (chk != VINF_OK) return chk;
     hipLaunchKernelGGL(conv3_gn_coeffs, dim3((C + 255) / 256), dim3(256), 0, st, mean, rstd, gamma, beta, C,
                        C / groups, pairs, a, b);
     const vinf_status r = run_conv3(x, ctx_pre, ctx_post, weight, bias, a, b, y, F, S, C, dt, st);
