@@ -82,6 +82,25 @@ vinf_status vinf_groupnorm_global(const void* x, void* y, const float* gamma, co
                                   size_t workspace_bytes, vinf_stream stream);
 
 /*
+ * vinf_groupnorm_global for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument and no allocation.  The workspace is a
+ * static device array of VINF_NOALLOC_SCRATCH_BYTES inside the library; each
+ * GPU the library runs on holds its own copy until the process ends.
+ * Arguments, limits and results are those of vinf_groupnorm_global (bit for
+ * bit); a shape whose workspace (vinf_groupnorm_workspace_bytes) exceeds
+ * VINF_NOALLOC_SCRATCH_BYTES returns VINF_ERR_UNSUPPORTED.  Every call on one
+ * GPU uses that GPU's array, so calls that overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller; a call
+ * writes every byte of it that it reads, so nothing needs clearing between
+ * calls.
+ */
+#define VINF_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+vinf_status vinf_groupnorm_global_noalloc(const void* x, void* y, const float* gamma, const float* beta,
+                                          float* mean_out, float* rstd_out, int F, int H, int W, int C,
+                                          int groups, float eps, vinf_dtype dt, vinf_stream stream);
+
+/*
  * Temporal convolution, kernel 3, with context padding (Conv-module
  * paragraph: convolution along the frame axis of each spatial location; the
  * clip is padded with the last frames of the previous clip and the first

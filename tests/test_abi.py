@@ -337,3 +337,30 @@ def test_broadcast_schedule_rejects(n, r):
     buf = ctypes.create_string_buffer(16)
     assert vinf.load().vinf_attn_broadcast_schedule(n, r, buf) == INVALID
     assert vinf.load().vinf_attn_broadcast_schedule(10, 2, None) == INVALID
+
+
+# ------------------------------------------ allocation-free GroupNorm entry point
+
+def gn_noalloc(**kw):
+    a = dict(x=A, y=B, gamma=None, beta=None, mean=None, rstd=None, F=16, H=8, W=5, C=64, G=8, eps=1e-5, dt=BF16)
+    a.update(kw)
+    return vinf.load().vinf_groupnorm_global_noalloc(a["x"], a["y"], a["gamma"], a["beta"], a["mean"], a["rstd"],
+                                                     a["F"], a["H"], a["W"], a["C"], a["G"], a["eps"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(x=A + 4), INVALID), (dict(gamma=Cp + 2), INVALID),
+    (dict(G=7), INVALID), (dict(F=0), INVALID), (dict(eps=-1.0), INVALID), (dict(dt=5), INVALID),
+    (dict(y=A + 64), INVALID),                           # partial overlap (only y == x is allowed)
+    (dict(mean=A + 128), INVALID),                       # statistics inside x
+    (dict(C=16384, G=32), UNSUPPORTED),                  # wider than the GroupNorm kernels take
+    # 2048 blocks x 4096 channels of fp32 partials = 32 MiB, more than the static scratch
+    (dict(F=64, H=64, W=64, C=4096, G=32, y=A), UNSUPPORTED),
+])
+def test_groupnorm_noalloc_rejects(kw, status):
+    assert gn_noalloc(**kw) == status
+
+
+def test_groupnorm_noalloc_limit_message():
+    assert gn_noalloc(F=64, H=64, W=64, C=4096, G=32, y=A) == UNSUPPORTED
+    assert b"scratch" in vinf.load().vinf_last_error()

@@ -36,7 +36,7 @@ import os
 
 import torch
 
-__all__ = ["groupnorm_global", "groupnorm_workspace_bytes", "temporal_conv3", "dual_domain_attn",
+__all__ = ["groupnorm_global", "groupnorm_global_noalloc", "groupnorm_workspace_bytes", "temporal_conv3", "dual_domain_attn",
            "groupnorm_clip_sums", "groupnorm_clip_apply", "dda_clip_halo", "dual_domain_attn_clip", "groupnorm_stats",
            "temporal_conv3_gn", "temporal_conv3_gn_workspace_bytes", "attn_broadcast_schedule",
            "dual_domain_attn_broadcast", "VinfError",
@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
                    "vinf_groupnorm_stats", "vinf_temporal_conv3_gn"):
             getattr(L, fn).restype = ctypes.c_int
         L.vinf_qkv_project.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.vinf_groupnorm_global_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.vinf_groupnorm_global_noalloc.restype = ctypes.c_int
         L.vinf_attn_broadcast_schedule.argtypes = [i, i, ctypes.c_char_p]
         L.vinf_attn_broadcast_schedule.restype = ctypes.c_int
         L.vinf_status_string.argtypes = [i]
@@ -211,6 +213,26 @@ def _ctx(ctx_pre, ctx_post, x: torch.Tensor) -> None:
             _same_device(c, x, name)
             if c.numel() != H * W * C or c.dtype != x.dtype:
                 raise ValueError(f"{name} must hold [H,W,C] = {H * W * C} values of {x.dtype}")
+
+
+def groupnorm_global_noalloc(x: torch.Tensor, groups: int, eps: float = 1e-5, gamma: torch.Tensor | None = None,
+                             beta: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                             mean_out: torch.Tensor | None = None, rstd_out: torch.Tensor | None = None, stream=None):
+    """groupnorm_global with the library's static scratch as its workspace (no
+    workspace argument, nothing allocated by the library).  Calls that overlap
+    on one GPU race.  Returns (y, mean[groups], rstd[groups])."""
+    _dev(x, "x")
+    F, H, W, C = _fhwc(x)
+    groups = int(groups)
+    y = _out_like(out, x)
+    mean = _vec_out(mean_out, x, "mean_out", groups)
+    rstd = _vec_out(rstd_out, x, "rstd_out", groups)
+    _vec(gamma, x, "gamma", C)
+    _vec(beta, x, "beta", C)
+    st = load().vinf_groupnorm_global_noalloc(_ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(mean), _ptr(rstd), F, H,
+                                              W, C, groups, float(eps), _dtype_code(x), _stream(x.device, stream))
+    _check("vinf_groupnorm_global_noalloc", st)
+    return y, mean, rstd
 
 
 def temporal_conv3(x: torch.Tensor, weight: torch.Tensor, ctx_pre: torch.Tensor | None = None,

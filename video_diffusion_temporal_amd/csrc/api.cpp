@@ -136,6 +136,32 @@ vinf_status vinf_groupnorm_global(const void* x, void* y, const float* gamma, co
                             (hipStream_t)stream);
 }
 
+vinf_status vinf_groupnorm_global_noalloc(const void* x, void* y, const float* gamma, const float* beta,
+                                          float* mean_out, float* rstd_out, int F, int H, int W, int C, int groups,
+                                          float eps, vinf_dtype dt, vinf_stream stream) {
+    const char* fn = "vinf_groupnorm_global_noalloc";
+    size_t bytes;
+    VINF_TRY(check_shape(fn, F, H, W, C, dt, &bytes));
+    VINF_TRY(check_tensor(fn, "x", x, true));
+    VINF_TRY(check_tensor(fn, "y", y, true));
+    VINF_TRY(check_f32(fn, "gamma", gamma));
+    VINF_TRY(check_f32(fn, "beta", beta));
+    VINF_TRY(check_f32(fn, "mean_out", mean_out));
+    VINF_TRY(check_f32(fn, "rstd_out", rstd_out));
+    if (groups < 1 || C % groups) return fail(VINF_ERR_INVALID_ARG, "%s: C=%d not divisible by groups=%d", fn, C, groups);
+    if (!(eps >= 0.f)) return fail(VINF_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+    const int vec = dt == VINF_BF16 ? 8 : 4;
+    if (C / vec > 1024) return fail(VINF_ERR_UNSUPPORTED, "%s: C=%d exceeds %d", fn, C, 1024 * vec);
+    if (y != x && overlap(x, bytes, y, bytes))
+        return fail(VINF_ERR_INVALID_ARG, "%s: y partially overlaps x (only y == x is allowed)", fn);
+    const size_t stat_bytes = (size_t)groups * sizeof(float);
+    if (overlap(mean_out, stat_bytes, x, bytes) || overlap(mean_out, stat_bytes, y, bytes) ||
+        overlap(rstd_out, stat_bytes, x, bytes) || overlap(rstd_out, stat_bytes, y, bytes))
+        return fail(VINF_ERR_INVALID_ARG, "%s: statistics overlap a tensor", fn);
+    return launch_groupnorm_noalloc(x, y, gamma, beta, mean_out, rstd_out, (int64_t)F * H * W, C, groups, eps, dt,
+                                    (hipStream_t)stream);
+}
+
 vinf_status vinf_groupnorm_stats(const void* x, float* mean_out, float* rstd_out, int F, int H, int W, int C,
                                  int groups, float eps, vinf_dtype dt, void* workspace, size_t workspace_bytes,
                                  vinf_stream stream) {

@@ -68,6 +68,11 @@ vinf_status launch_groupnorm(const void* x, void* y, const float* gamma, const f
                              float* rstd_out, int64_t rows, int C, int groups, float eps, vinf_dtype dt,
                              void* workspace, hipStream_t stream);
 size_t groupnorm_workspace(int64_t rows, int C, int groups, vinf_dtype dt);
+// The same with the library's static scratch array as the workspace (sizes
+// needing more than VINF_NOALLOC_SCRATCH_BYTES are rejected).
+vinf_status launch_groupnorm_noalloc(const void* x, void* y, const float* gamma, const float* beta, float* mean_out,
+                                     float* rstd_out, int64_t rows, int C, int groups, float eps, vinf_dtype dt,
+                                     hipStream_t stream);
 // One clip's fp64 group sums (first pass: mean_sums null; second pass: about
 // the means mean_sums[g] / n_total).
 vinf_status launch_groupnorm_clip_sums(const void* x, const double* mean_sums, double* sums, int64_t rows, int C,

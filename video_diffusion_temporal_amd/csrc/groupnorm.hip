@@ -34,9 +34,16 @@
 // covering the whole video reproduces the whole-video path bit for bit.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace vinf {
+
+// Scratch of vinf_groupnorm_global_noalloc: the per-block partial sums and
+// the statistics of one call, in a static device array instead of a
+// caller-provided workspace.  Every call on a GPU uses that GPU's copy.
+static __device__ __align__(256) char scratch[VINF_NOALLOC_SCRATCH_BYTES];
 
 constexpr int GN_MAX_BLOCKS = 2048;
 
@@ -348,6 +355,42 @@ vinf_status launch_groupnorm(const void* x, void* y, const float* gamma, const f
     if (dt == VINF_BF16)
         return run<true>(x, y, gamma, beta, mean_out, rstd_out, rows, C, groups, eps, workspace, stream);
     return run<false>(x, y, gamma, beta, mean_out, rstd_out, rows, C, groups, eps, workspace, stream);
+}
+
+// The device address of the scratch array on the current device, looked up
+// once per device (the array's name in host code is not a device address).
+static vinf_status scratch_address(void** out) {
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static void* addr[MAX_DEVICES] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+        return fail(VINF_ERR_HIP, "groupnorm_noalloc: no current device (or more than %d)", MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(VINF_ERR_HIP, "groupnorm_noalloc: hipGetSymbolAddress failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return VINF_OK;
+}
+
+vinf_status launch_groupnorm_noalloc(const void* x, void* y, const float* gamma, const float* beta, float* mean_out,
+                                     float* rstd_out, int64_t rows, int C, int groups, float eps, vinf_dtype dt,
+                                     hipStream_t stream) {
+    const size_t need = groupnorm_workspace(rows, C, groups, dt);
+    if (need > VINF_NOALLOC_SCRATCH_BYTES)
+        return fail(VINF_ERR_UNSUPPORTED,
+                    "vinf_groupnorm_global_noalloc: C=%d needs %zu bytes of scratch, more than the %zu the library holds",
+                    C, need, (size_t)VINF_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const vinf_status r = scratch_address(&ws);
+    if (r != VINF_OK) return r;
+    return launch_groupnorm(x, y, gamma, beta, mean_out, rstd_out, rows, C, groups, eps, dt, ws, stream);
 }
 
 vinf_status launch_groupnorm_clip_sums(const void* x, const double* mean_sums, double* sums, int64_t rows, int C,
