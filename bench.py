@@ -73,8 +73,29 @@ def traffic_record(kernel):
     return rec.get("bytes_per_launch")
 
 
+def host_threads():
+    """Host threads this process may run on: its CPU affinity set, further
+    limited by a cgroup CPU quota when one is set.  Returns (threads, detail)."""
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = nproc
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+            if q != "max":
+                quota = max(1, int(int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    threads = min(affinity, quota) if quota else affinity
+    return threads, {"nproc": nproc, "affinity": affinity, "cgroup_quota_cpus": quota}
+
+
 def cpu_baseline(F, C, G, side=16):
-    """The oracle chain, as it stands, on F frames x side x side locations."""
+    """The oracle chain, as it stands, on F frames x side x side locations,
+    over every host thread this process may use."""
     import numpy as np
 
     import oracle
@@ -83,7 +104,7 @@ def cpu_baseline(F, C, G, side=16):
     H = W = side
     x = synth.make_tensor(SEED_CONFIG, synth.X_GN, F, H, W, C, synth.BF16)
     w = synth.make_conv_weight(SEED_CONFIG, C, synth.BF16)
-    threads = min(os.cpu_count() or 1, 16)
+    threads, detail = host_threads()
     t = time.perf_counter()
     oracle.chain(x, w, G, nthreads=threads)
     dt = time.perf_counter() - t
@@ -91,7 +112,7 @@ def cpu_baseline(F, C, G, side=16):
     return {"value": vox / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
             "sample": f"oracle chain (GroupNorm stats+apply, conv3, attention) in fp64 on F={F}, "
                       f"{H}x{W} locations, C={C}: {vox} voxels in {dt:.2f} s",
-            "seconds": dt, "cpu_model": cpu_model()}
+            "seconds": dt, "cpu_model": cpu_model(), "host": detail}
 
 
 def cpu_model():
@@ -410,6 +431,11 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic_record(dom)}
     roof["ms_per_launch"] = round(mod_ms[dom], 4)
+    # The HBM bytes the counters saw per launch, over the same time and peak:
+    # for the attention with Q = K = V one tensor is read once, not three times.
+    if roof["traffic"]:
+        roof["physical_gbs"] = round(roof["traffic"] / (mod_ms[dom] * 1e-3) / 1e9, 1)
+        roof["physical_frac"] = round(roof["physical_gbs"] / HBM_PEAK_GBS, 4)
 
     # Attention on three distinct tensors (in the chain Q, K and V are one
     # tensor, so that call reads half the bytes a general call must).

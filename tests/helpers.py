@@ -140,3 +140,86 @@ def check_end_to_end(got, out, o_on_gpu_conv, cv_r, cs, dt, what):
     assert err.mean() <= mean_tol, f"{what}: end-to-end mean-abs {err.mean():.3e} (<= {mean_tol})"
     assert rest <= max_tol, f"{what}: end-to-end max-abs {rest:.3e} (<= {max_tol})"
     assert np.all(err <= max_tol + allow), f"{what}: end-to-end beyond the allowance ({(err - max_tol - allow).max():.3e})"
+
+
+U_BF16 = 2.0 ** -8  # unit roundoff of bf16 (8-bit significand, round to nearest even)
+U_F32 = 2.0 ** -24
+
+
+def ulp_bf16(a: np.ndarray) -> np.ndarray:
+    """The spacing of bf16 values at |a| (2^(e-7) for |a| in [2^e, 2^(e+1)))."""
+    m, e = np.frexp(np.abs(a))   # |a| = m * 2^e, m in [0.5, 1)
+    return np.where(a == 0, 0.0, np.ldexp(1.0, e - 8))
+
+
+def check_ulp(got: np.ndarray, ref: np.ndarray, err_term: np.ndarray, what: str):
+    """Per element |got - ref| <= half a bf16 ulp (the output rounding) plus
+    the kernel's own error term."""
+    half = 0.5 * ulp_bf16(np.maximum(np.abs(got), np.abs(ref)))
+    err = np.abs(got - ref)
+    slack = err - (half + err_term)
+    within_half = float(np.mean(err <= half))
+    print(f"  {what}: max |err| / (half-ulp + term) = {float((err / (half + err_term + 1e-300)).max()):.3f}; "
+          f"{within_half:.4f} of outputs within half an ulp alone; largest term {float(err_term.max()):.2e}",
+          flush=True)
+    assert np.all(slack <= 0), (f"{what}: {int((slack > 0).sum())} outputs beyond half an ulp + the kernel term "
+                                f"(worst excess {float(slack.max()):.3e})")
+
+
+def attention_terms(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float = 0.125, head_dim: int = 64,
+                    eps_w: float = 1e-4):
+    """For attention over [F, n, C] float64 q, k, v (Q/K/V at n locations): the
+    exact output o and the per-element error term of a kernel that rounds each
+    softmax weight to bf16 and normalises by the sum of the rounded weights.
+
+    Each rounded weight is p_j e^(eta_j) with |eta_j| <= U_BF16 + eps_w (eps_w
+    covers the fp32 scores and exp2), so the normalised weights move by a
+    factor within e^(+-2 eta) and the output by at most
+        (e^(2 eta) - 1) * sum_j pi_j |v_j - o|        (pi: exact weights)
+    plus the fp32 sums of 34 products and 17 weights and the final
+    normalisation, at most 64 U_F32 (max_j |v_j| + |o|).  Also returns the
+    largest score magnitude sum_d |q_d k_d| over the sample (eps_w holds while
+    it stays below 1000)."""
+    F, n, C = q.shape
+    H = C // head_dim
+    qh = q.reshape(F, n, H, head_dim)
+    kh = k.reshape(F, n, H, head_dim)
+    vh = v.reshape(F, n, H, head_dim)
+    o = np.empty_like(qh)
+    term = np.empty_like(qh)
+    smax = 0.0
+    eta = U_BF16 + eps_w
+    for t in range(F):
+        J = np.array(key_frames(t, F))                                     # 32 keys, repeats kept
+        s = scale * np.einsum("nhd,jnhd->jnh", qh[t], kh[J])
+        smax = max(smax, float(np.einsum("nhd,jnhd->jnh", np.abs(qh[t]), np.abs(kh[J])).max()))
+        p = np.exp(s - s.max(axis=0, keepdims=True))
+        pi = p / p.sum(axis=0, keepdims=True)                              # [32, n, H]
+        ot = np.einsum("jnh,jnhd->nhd", pi, vh[J])
+        spread = np.einsum("jnh,jnhd->nhd", pi, np.abs(vh[J] - ot[None]))
+        vmax = np.abs(vh[J]).max(axis=0)
+        o[t] = ot
+        term[t] = np.expm1(2 * eta) * spread + 64 * U_F32 * (vmax + np.abs(ot))
+    return o.reshape(F, n, C), term.reshape(F, n, C), smax
+
+
+def conv_terms(x_abs_conv: np.ndarray, C: int) -> np.ndarray:
+    """Error term of a kernel-3 conv accumulated in fp32 from exact bf16
+    products: at most 3C + 2 roundings along any summation path, each within
+    U_F32 of a partial sum bounded by sum |W| |x| (x_abs_conv: that sum, the
+    conv of |x| with |W|)."""
+    return (3 * C + 2) * U_F32 * x_abs_conv
+
+
+def groupnorm_terms(x: np.ndarray, mean: np.ndarray, rstd: np.ndarray, G: int, d_mean: float = 1e-5,
+                    d_rstd: float = 1e-5) -> np.ndarray:
+    """Error term of y = fma(x, a, b) in fp32 with a = rstd_g and b = -mean_g a
+    formed in fp32 from statistics within d_mean (absolute) and d_rstd
+    (relative) of the exact ones (the stats tests assert those bounds):
+        |x a + b - (x - mean) rstd| <= rstd (|x| (d_rstd + U) + d_mean + |mean| (d_rstd + 2U))
+    plus the fma's own rounding, U |y|.  x: [F, n, C] float64; mean, rstd: [G]."""
+    C = x.shape[-1]
+    m = np.repeat(mean, C // G)
+    r = np.repeat(rstd, C // G)
+    y = (x - m) * r
+    return r * (np.abs(x) * (d_rstd + U_F32) + d_mean + np.abs(m) * (d_rstd + 2 * U_F32)) + U_F32 * np.abs(y)
