@@ -37,7 +37,8 @@
 //     with scheduling-group hints; the compiler otherwise reads them just
 //     before use).  The weight fragment is the MFMA's A operand, so
 //     each lane's accumulator holds 4 consecutive output channels of one
-//     voxel.  The epilogue swaps fragment pairs across lane groups
+//     voxel, and starts from the bias of those channels.  The epilogue
+//     rounds and swaps fragment pairs across lane groups
 //     (v_permlane32_swap, v_permlane16_swap) so that a lane holds 8
 //     consecutive channels and writes 16-byte pieces (64 contiguous bytes of
 //     a voxel row per store instruction).
@@ -191,11 +192,29 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         }
     };
 
+    // Accumulators, started from the bias of the lane's channels (4
+    // consecutive channels per fragment, the same for every mi) or zeros.
     f32x4_t acc[4][NF];
+    auto acc_init = [&](int t) {
+        // lane values from an opaque copy of the lane id, so that nothing of
+        // this stays live (hoisted) through the MFMA stages
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int lc = el >> 4;
+        const int n0 = (t % ntn) * BN;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+        for (int ni = 0; ni < NF; ++ni) {
+            f32x4_t b = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (bias) {
+                // channel n of the N range (q, k, v rows for the projection) = bias[n]
+                const float* bp = bias + n0 + wn * 16 * NF + ni * 16 + 4 * lc;
+                b = f32x4_t{bp[0], bp[1], bp[2], bp[3]};
+            }
 #pragma unroll
-        for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mi = 0; mi < 4; ++mi) acc[mi][ni] = b;
+        }
+    };
+    if (t_begin < t_end) acc_init(t_begin);
 
     // GroupNorm.  gn_ab is a table of channel pairs, 16 bytes each (a_2p,
     // a_2p+1, b_2p, b_2p+1), so a slice's coefficients are 256 contiguous
@@ -350,6 +369,9 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         // of output n0 / C (BN divides C, so a tile stays in one output).
         int f0, s0, n0;
         tile_coords(t, f0, s0, n0);
+        int el = lane;  // opaque lane id: nothing derived from it is hoisted into the stages
+        asm volatile("" : "+v"(el));
+        const int lr = el & 15, lc = el >> 4;
         const int s = s0 + lr;
         const int po = TAPS == 3 ? 0 : n0 / C;
         uint16_t* yo = TAPS == 3 ? y : (po == 0 ? y : (po == 1 ? y1 : y2));
@@ -359,9 +381,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         // 8g .. 8g+7 of the pair (g = 0, 1 from fragment ni, g = 2, 3 from
         // ni+1), so each store covers 64 contiguous bytes of a voxel row.
         auto packed = [&](int mi, int ni, int half) {
-            const int n = n0 + wn * 16 * NF + ni * 16 + 4 * lc + 2 * half;
-            const float b0 = bias ? bias[n] : 0.f, b1 = bias ? bias[n + 1] : 0.f;
-            return pack_bf16x2(acc[mi][ni][2 * half] + b0, acc[mi][ni][2 * half + 1] + b1);
+            return pack_bf16x2(acc[mi][ni][2 * half], acc[mi][ni][2 * half + 1]);
         };
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -376,16 +396,25 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
                 const int nb = n0 + wn * 16 * NF + np * 16 + 8 * lc;
                 if (f < F && s < S)
                     *reinterpret_cast<u32x4_t*>(yo + row + nb) = u32x4_t{lo[0], hi[0], lo[1], hi[1]};
+                // Projection: each store completes before the next.  Its tiles
+                // write as many bytes as they read in five stages; released at
+                // once, the writes hold up the next stages' loads (measured:
+                // about 10% slower overall than stores one at a time).
+                if constexpr (TAPS == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             }
             if constexpr (NF & 1) {
                 const int ni = NF - 1;
                 const int n = n0 + wn * 16 * NF + ni * 16 + 4 * lc;
                 const uint2 o = {packed(mi, ni, 0), packed(mi, ni, 1)};
                 if (f < F && s < S) *reinterpret_cast<uint2*>(yo + row + n) = o;
+                if constexpr (TAPS == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             }
-#pragma unroll
-            for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+        // The next tile starts from its bias.  These loads go out after the
+        // stores and are first needed after the next stage's wait, so nothing
+        // waits on them here (a load between stores would make its wait, on a
+        // counter that also counts stores, wait for every store before it).
+        if (t + 1 < t_end) acc_init(t + 1);
     }
 }
 
