@@ -151,20 +151,32 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         n0 = nt * BN;
     };
 
-    // Issue the loads of slices kc .. kc+KS-1 of tile t into buffer b.
-    auto issue = [&](int t, int kc0, int b) {
-        int f0, s0, n0;
-        tile_coords(t, f0, s0, n0);
+    // Stage cursor: tile ti, slice ki of the next stage to issue, and ti's
+    // coordinates (computed once per tile: tile_coords divides).
+    int ti = t_begin, ki = 0;
+    int cf0 = 0, cs0 = 0, cn0 = 0;
+    auto cursor_tile = [&]() { tile_coords(ti, cf0, cs0, cn0); };
+
+    // Issue the loads of slices kc0 .. kc0+KS-1 of the cursor tile into
+    // buffer b.  The slice is the instructions' scalar offset (kc * 64 bytes);
+    // per lane there are two offsets, formed here from an opaque copy of the
+    // lane id (kept live through the stages they would cost registers).
+    auto issue = [&](int kc0, int b) {
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int srow = el >> 2, schunk = (el & 3) ^ ((el >> 3) & 3);
+        // x: the lane's location row of a frame, or past the end (zeros)
+        const uint32_t xvoff = cs0 + srow < S ? ((uint32_t)(cs0 + srow) * (uint32_t)C + (uint32_t)(schunk * 8)) * 2u
+                                              : frame_bytes;
+        // weights: the lane's row of a 16-row block
+        const uint32_t wlane = ((uint32_t)srow * (uint32_t)C + (uint32_t)(schunk * 8)) * 2u;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int kc = kc0 + ks;
+            const uint32_t soff = (uint32_t)((kc0 + ks) * CV_BK) * 2u;
             char* abuf = lds + b * L::BUF + ks * L::SLOT;
             char* bbuf = abuf + L::A_BYTES;
-            const uint32_t loc_off =
-                ((uint32_t)(s0 + st_row) * (uint32_t)C + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
-            const uint32_t voff = s0 + st_row < S ? loc_off : frame_bytes;   // past the end: zeros
             for (int i = wv; i < NSTG; i += NW) {                           // one frame per instruction
-                const int f = f0 - HALO + i;
+                const int f = cf0 - HALO + i;
                 const void* base = x;
                 uint32_t nrec = 0;
                 if (f >= 0 && f < F) {
@@ -179,18 +191,18 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
                 }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(cv_rsrc(base, nrec),
                                                          (__attribute__((address_space(3))) void*)(abuf + i * 1024), 16,
-                                                         voff, 0, 0, 0);
+                                                         xvoff, soff, 0, 0);
             }
             for (int i = wv; i < B_INSTR; i += NW) {                        // 16 weight rows per instruction
-                const int r = 16 * i + st_row;                              // r = tap*BN + co (tap 0 when TAPS = 1)
-                const int tap = r / BN, co = r - tap * BN;
-                const uint32_t off =
-                    ((uint32_t)((tap * C + n0 + co) * C) + (uint32_t)(kc * CV_BK + st_chunk * 8)) * 2u;
+                // rows 16i .. 16i+15 = tap*BN + co0 + 0..15 (16 divides BN)
+                const int tap = i / (BN / 16), co0 = 16 * (i - tap * (BN / 16));
+                const uint32_t wsoff = (uint32_t)((tap * C + cn0 + co0) * C) * 2u + soff;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(bbuf + i * 1024),
-                                                         16, off, 0, 0, 0);
+                                                         16, wlane, wsoff, 0, 0);
             }
         }
     };
+
 
     // Accumulators, started from the bias of the lane's channels (4
     // consecutive channels per fragment, the same for every mi) or zeros.
@@ -257,11 +269,9 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         *reinterpret_cast<uint32_t*>(blk + g_even + 512) = v[2];
         *reinterpret_cast<uint32_t*>(blk + g_odd + 768) = v[3];
     };
-    // All frame blocks this wave loaded for stage (t, slot) in buffer buf, from
-    // block index i0 on.
-    auto gn_blocks = [&](int t, int buf, int slot, int i0) {
-        int f0, s0, n0;
-        tile_coords(t, f0, s0, n0);
+    // All frame blocks this wave loaded for a stage of the tile whose first
+    // frame is f0 (coefficient slot slot, buffer buf), from block index i0 on.
+    auto gn_blocks = [&](int f0, int buf, int slot, int i0) {
         for (int i = i0; i < NSTG; i += NW) {
             char* blk = lds + buf * L::BUF + i * 1024;
             uint32_t u[4];
@@ -271,17 +281,17 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         }
     };
 
-    // Stage cursor: tile ti, slice ki of the next stage to issue.
-    int ti = t_begin, ki = 0;
     auto issue_next = [&](int buf) {
-        issue(ti, ki, buf);
+        issue(ki, buf);
         ki += KS;
         if (ki >= nk) {
             ki = 0;
             ++ti;
+            if (ti < t_end) cursor_tile();
         }
     };
     if (t_begin < t_end) {
+        cursor_tile();
         issue_next(0);
         ab_issue(0, 0);    // stage 0
         ab_issue(ki, 1);   // stage 1
@@ -290,7 +300,11 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         if (tid < 4) reinterpret_cast<uint32_t*>(ab_lds + 512)[tid] = 0u;
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();                      // the coefficients of stages 0 and 1 and the zero slot
-        if (t_begin < t_end) gn_blocks(t_begin, 0, 0, wv);
+        if (t_begin < t_end) {
+            int f0, s0, n0;
+            tile_coords(t_begin, f0, s0, n0);
+            gn_blocks(f0, 0, 0, wv);
+        }
     }
     int g = 0;  // stage counter across tiles (selects the buffer)
     for (int t = t_begin; t < t_end; ++t) {
@@ -299,7 +313,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
             // for, and normalised, while stage g-1 was multiplied).
             if constexpr (!GN) __builtin_amdgcn_s_waitcnt(0x0f70);
             __syncthreads();                      // everyone's are; stage g-1 is no longer read
-            const int t_next = ti;                // the tile of stage g+1, if there is one
+            const int f0_next = cf0;              // first frame of the tile of stage g+1, if there is one
             if (ti < t_end) issue_next((g + 1) & 1);
             ab_issue(ki, g & 1);                  // GN: the coefficients of stage g+2
             // GN: stage g+1 is normalised in the shadow of stage g's last MFMA
@@ -308,11 +322,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
             // Past the last stage this rewrites a buffer no one reads again.
             char* const nbuf = lds + ((g + 1) & 1) * L::BUF;
             bool n_live = false;
-            if constexpr (GN) {
-                int f0, s0, n0;
-                tile_coords(t_next, f0, s0, n0);
-                n_live = frame_live(f0 - HALO + wv);
-            }
+            if constexpr (GN) n_live = frame_live(f0_next - HALO + wv);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const char* abuf = lds + (g & 1) * L::BUF + ks * L::SLOT;
@@ -362,7 +372,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
             }
             // GN: a wave's further blocks (NSTG > NW: the first NSTG - NW waves).
             if constexpr (GN && NSTG > NW)
-                if (wv + NW < NSTG) gn_blocks(t_next, (g + 1) & 1, (g + 1) & 1, wv + NW);
+                if (wv + NW < NSTG) gn_blocks(f0_next, (g + 1) & 1, (g + 1) & 1, wv + NW);
         }
         // Epilogue: fragment (mi, ni) holds frame f0 + 4*wm + mi, location
         // s0 + lane%16, channels n0 + wn*16*NF + ni*16 + 4*(lane/16) + 0..3
