@@ -224,7 +224,8 @@ def next_rows(vinf, x, cv, G, stream, steps):
     frames and the 16 gathered global rows, as one device of an 8-way clip
     split would run it.  Ablations: the local-only and global-only key sets at
     F=1024 on the chain's conv output (Q = K = V).  Projection: Q, K and V as
-    three C x C maps of the conv output's tokens, and the attention over them."""
+    three C x C maps of the conv output's tokens, and the attention over them,
+    as two calls and as one fused call."""
     import numpy as np
     import torch
 
@@ -292,6 +293,10 @@ def next_rows(vinf, x, cv, G, stream, steps):
     ms = timed(lambda: vinf.projected_dual_domain_attn(cv, wq, out=o, qkv=qkv, stream=stream), steps, stream)
     out["projected_dda_bf16"] = {"ms": round(ms, 4), "voxels_per_s": F * S / (ms * 1e-3),
                                  "shape": f"F={F}, {H}x{W}x{C}: qkv_project, then dual_domain_attn on q, k, v"}
+    ms = timed(lambda: vinf.projected_dual_domain_attn_fused(cv, wq, out=o, stream=stream), steps, stream)
+    out["projected_dda_bf16_fused"] = {"ms": round(ms, 4), "voxels_per_s": F * S / (ms * 1e-3),
+                                       "shape": f"F={F}, {H}x{W}x{C}: one launch, q, k, v projected inside the "
+                                                f"attention's work items and never written"}
     del qkv, o
     # Reuse of attention outputs across a 30-step sampling schedule (range 3):
     # the attention cost per diffusion step, averaged over the schedule.

@@ -218,6 +218,32 @@ vinf_status vinf_qkv_project(const void* x, const void* weight, const float* bia
                              int F, int H, int W, int C, vinf_dtype dt, vinf_stream stream);
 
 /*
+ * Dual-domain attention over projected tokens, with the projection inside the
+ * attention's work items (dual-domain attention paragraph: the query token
+ * comes from frame t, and the keys and values are computed from the tokens
+ * of its frame set).  The result is that of
+ *
+ *   vinf_qkv_project(x, weight, bias, q, k, v, ...)
+ *   vinf_dual_domain_attn(q, k, v, o, ..., n_local = 16, n_global = 16, scale)
+ *
+ * bit for bit (the same bf16 rounding of q, k and v), but q, k and v are
+ * never written: each work item (one location, one head, 256 query frames)
+ * projects the rows of x its windows and the 16 global frames need, on the
+ * matrix cores, straight into the attention's LDS layout.
+ *
+ * x, o      [F][H][W][C] bf16; o must not overlap x, weight or bias.
+ * weight    [3][C_out=C][C_in=C] bf16 (the q, k and v maps).
+ * bias      [3][C] float32 or NULL.
+ * scale     <= 0 selects 1/sqrt(head_dim).
+ * Limits    bf16 only, head_dim == 64, C % 64 == 0, n_local == n_global == 16
+ *           (anything else: VINF_ERR_UNSUPPORTED; the two calls above cover
+ *           float32 and the ablation key sets).
+ */
+vinf_status vinf_projected_dual_domain_attn(const void* x, const void* weight, const float* bias, void* o, int F,
+                                            int H, int W, int C, int head_dim, int n_local, int n_global, float scale,
+                                            vinf_dtype dt, vinf_stream stream);
+
+/*
  * GroupNorm of one clip with statistics over the whole video (the clip-
  * parallelism paragraph: each device holds a clip and its temporal modules
  * exchange context; for GroupNorm the context is the aggregated statistics

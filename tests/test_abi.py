@@ -36,7 +36,7 @@ def test_exports_every_declared_function():
     assert set(names) >= {"vinf_groupnorm_global", "vinf_temporal_conv3", "vinf_dual_domain_attn",
                           "vinf_groupnorm_workspace_bytes", "vinf_status_string", "vinf_last_error",
                           "vinf_groupnorm_clip_sums", "vinf_groupnorm_clip_apply", "vinf_dda_clip_halo",
-                          "vinf_dual_domain_attn_clip", "vinf_qkv_project"}
+                          "vinf_dual_domain_attn_clip", "vinf_qkv_project", "vinf_projected_dual_domain_attn"}
     lib = ctypes.CDLL(vinf.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -130,6 +130,30 @@ def test_qkv_project_rejects(kw, status):
     assert vinf.load().vinf_last_error()
 
 
+def pattn(**kw):
+    a = dict(x=A, w=B, bias=None, o=Cp, F=16, H=8, W=5, C=64, hd=64, nl=16, ng=16, scale=0.0, dt=BF16)
+    a.update(kw)
+    return vinf.load().vinf_projected_dual_domain_attn(a["x"], a["w"], a["bias"], a["o"], a["F"], a["H"], a["W"],
+                                                       a["C"], a["hd"], a["nl"], a["ng"], a["scale"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(o=None), INVALID),
+    (dict(x=A + 4), INVALID), (dict(o=Cp + 8), INVALID), (dict(bias=D + 2), INVALID),
+    (dict(F=0), INVALID), (dict(H=0), INVALID), (dict(dt=5), INVALID),
+    (dict(C=96), INVALID),                        # not a multiple of head_dim
+    (dict(hd=32), UNSUPPORTED),
+    (dict(dt=F32), UNSUPPORTED),                  # bf16 only
+    (dict(nl=0), UNSUPPORTED), (dict(ng=0), UNSUPPORTED),   # the full key set only
+    (dict(scale=float("nan")), INVALID),
+    (dict(o=A), INVALID), (dict(o=A + 16 * 40 * 64 * 2 - 16), INVALID),   # o overlaps x
+    (dict(o=B + 64), INVALID), (dict(bias=D, o=D + 128), INVALID),       # o overlaps weight / bias
+])
+def test_projected_attention_rejects(kw, status):
+    assert pattn(**kw) == status
+    assert vinf.load().vinf_last_error()
+
+
 def gn(**kw):
     L = vinf.load()
     a = dict(x=A, y=B, gamma=None, beta=None, mean=None, rstd=None, F=16, H=8, W=5, C=64, G=8, eps=1e-5, dt=F32,
@@ -167,6 +191,8 @@ def test_python_binding_requires_gpu_tensors():
         vinf.groupnorm_global(x, 8)
     with pytest.raises(TypeError):
         vinf.qkv_project(x, torch.zeros(3, 64, 64))
+    with pytest.raises(TypeError):
+        vinf.projected_dual_domain_attn_fused(x, torch.zeros(3, 64, 64))
 
 
 # ------------------------------------------------------------ clip forms

@@ -68,7 +68,8 @@ BAD_OUT = {
 
 @pytest.mark.parametrize("bad", sorted(BAD_OUT))
 @pytest.mark.parametrize("call", ["groupnorm_global", "temporal_conv3", "dual_domain_attn", "temporal_conv3_gn",
-                                  "groupnorm_clip_apply", "dual_domain_attn_clip", "qkv_project"])
+                                  "groupnorm_clip_apply", "dual_domain_attn_clip", "qkv_project",
+                                  "projected_dual_domain_attn_fused"])
 def test_bad_output_tensor_raises_before_launch(lib, call, bad):
     x = x_()
     out = BAD_OUT[bad]()
@@ -87,6 +88,8 @@ def test_bad_output_tensor_raises_before_launch(lib, call, bad):
             vinf.groupnorm_clip_apply(x, G, F, s, s, out=out)
         elif call == "dual_domain_attn_clip":
             vinf.dual_domain_attn_clip(x, x, x, F, 0, 0, 0, out=out)
+        elif call == "projected_dual_domain_attn_fused":
+            vinf.projected_dual_domain_attn_fused(x, wt, out=out)
         else:
             vinf.qkv_project(x, wt, out=(x_(), out, x_()))
     assert launched(lib) == []
@@ -154,6 +157,10 @@ def test_conv3_vectors(lib, field, value):
 def test_qkv_project_bias(lib):
     with pytest.raises(ValueError):
         vinf.qkv_project(x_(), torch.zeros(3, C, C, dtype=BF), bias=f32(C))
+    with pytest.raises(ValueError):
+        vinf.projected_dual_domain_attn_fused(x_(), torch.zeros(3, C, C, dtype=BF), bias=f32(C))
+    with pytest.raises(ValueError):
+        vinf.projected_dual_domain_attn_fused(x_(), torch.zeros(3, C, C, dtype=torch.float32))
     assert launched(lib) == []
 
 
@@ -176,6 +183,8 @@ def test_good_arguments_reach_the_library(lib):
     vinf.groupnorm_clip_sums(x, G, F, out=torch.zeros(G, dtype=torch.float64))
     vinf.groupnorm_clip_apply(x, G, F, s, s, gamma=f32(C), out=x_(), mean_out=f32(G), rstd_out=f32(G))
     vinf.dual_domain_attn_clip(x, x, x, F, 0, 0, 0, out=x_())
+    vinf.projected_dual_domain_attn_fused(x, wt, bias=f32(3 * C), out=x_())
     assert launched(lib) == ["vinf_groupnorm_global", "vinf_groupnorm_stats", "vinf_temporal_conv3",
                              "vinf_temporal_conv3_gn", "vinf_dual_domain_attn", "vinf_qkv_project",
-                             "vinf_groupnorm_clip_sums", "vinf_groupnorm_clip_apply", "vinf_dual_domain_attn_clip"]
+                             "vinf_groupnorm_clip_sums", "vinf_groupnorm_clip_apply", "vinf_dual_domain_attn_clip",
+                             "vinf_projected_dual_domain_attn"]

@@ -7,6 +7,10 @@ oracle's exact projection at the bar (ragged frame and location tiles, every
 tile width the kernel has), identity maps bit for bit, and the attention over
 the projected tokens in two stages (projection vs the oracle; attention over
 the GPU's own Q/K/V vs the oracle's attention), as the chain tests do.
+
+The fused call (projection inside the attention's work items) must give the
+two calls' result bit for bit: it rounds the same fp32 sums, accumulated in
+the same order, to the same bf16 q, k and v.
 """
 import numpy as np
 import pytest
@@ -125,3 +129,39 @@ def test_projected_attention_at_workload_size():
         check(cols[p], exact[p], BF, "qkv"[p] + " (sampled locations)")
     gq, gk, gv = (to_bf16_bits(c).reshape(F, len(locs), 1, C) for c in cols)
     check(fetch(o, locs), oracle.dda(gq, gk, gv), BF, "attention over the GPU's q, k, v (sampled locations)")
+
+
+@pytest.mark.parametrize("F,H,W,C,bias", [
+    (37, 5, 7, 320, True),     # one partial 256-frame item per strip
+    (300, 2, 3, 128, False),   # a full and a partial item per strip
+    (513, 1, 2, 64, True),     # three items per strip, one query in the last
+    (5, 2, 2, 64, True),       # F < 16: every frame is local context, rows past F are zeros
+    (16, 3, 3, 192, False),    # F = 16: one window, global frames 0 .. 15
+    (40, 4, 5, 640, True),     # ten heads
+])
+def test_fused_projected_attention(F, H, W, C, bias):
+    announce(f"fused projected attention F={F} H={H} W={W} C={C} bias={bias}")
+    x = rnd((F, H, W, C), 6500 + F, BF)
+    w = rnd((3, C, C), 6501 + C, BF, (1.0 / C) ** 0.5)
+    b = np.linspace(-0.2, 0.2, 3 * C).astype(np.float32).reshape(3, C) if bias else None
+    xd, wd = upload(x), upload(w)
+    bd = None if b is None else torch.from_numpy(b).to(dev())
+    o = vinf.projected_dual_domain_attn_fused(xd, wd, bd)
+    q, k, v = vinf.qkv_project(xd, wd, bd)
+    assert np.array_equal(bits(o), bits(vinf.dual_domain_attn(q, k, v))), "fused != qkv_project + attention"
+    gq, gk, gv = (to_bf16_bits(fetch(t).reshape(F, H, W, C)) for t in (q, k, v))
+    check(fetch(o), oracle.dda(gq, gk, gv), BF, "fused: attention over the projected q, k, v vs the oracle")
+    exact = oracle.qkv_project(x, w, None if b is None else b.astype(np.float64))
+    check(fetch(k), exact[1], BF, "k vs the oracle's projection")
+
+
+def test_fused_projected_attention_at_workload_size():
+    F, H, W, C = 1024, 64, 40, 320
+    announce(f"fused projected attention at workload size F={F} {H}x{W}x{C} bf16")
+    cfg = 6
+    xd = upload(synth.make_tensor(cfg, synth.X_CONV, F, H, W, C, BF))
+    wd = upload(synth.make_qkv_weight(cfg, C, BF))
+    b = torch.linspace(-0.1, 0.1, 3 * C, device=dev())
+    o = vinf.projected_dual_domain_attn_fused(xd, wd, b)
+    ref = vinf.projected_dual_domain_attn(xd, wd, b)
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), "fused != qkv_project + attention"

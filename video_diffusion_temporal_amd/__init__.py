@@ -83,6 +83,7 @@ def load() -> ctypes.CDLL:
                    "vinf_groupnorm_stats", "vinf_temporal_conv3_gn"):
             getattr(L, fn).restype = ctypes.c_int
         L.vinf_qkv_project.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.vinf_projected_dual_domain_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
         L.vinf_groupnorm_global_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         L.vinf_groupnorm_global_noalloc.restype = ctypes.c_int
         L.vinf_attn_broadcast_schedule.argtypes = [i, i, ctypes.c_char_p]
@@ -304,6 +305,25 @@ def projected_dual_domain_attn(x: torch.Tensor, weight: torch.Tensor, bias: torc
     q, k, v = qkv_project(x, weight, bias, out=qkv, stream=stream)
     return dual_domain_attn(q, k, v, out=out, head_dim=head_dim, n_local=n_local, n_global=n_global, scale=scale,
                             stream=stream)
+
+
+def projected_dual_domain_attn_fused(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                                     out: torch.Tensor | None = None, head_dim: int = 64, scale: float = 0.0,
+                                     stream=None) -> torch.Tensor:
+    """The same result as projected_dual_domain_attn (full key set, bf16), in one
+    launch that never writes q, k and v (vinf_projected_dual_domain_attn)."""
+    _dev(x, "x")
+    _dev(weight, "weight")
+    F, H, W, C = _fhwc(x)
+    if tuple(weight.shape) != (3, C, C) or weight.dtype != x.dtype:
+        raise ValueError(f"weight must be [3,{C},{C}] of {x.dtype}")
+    _same_device(weight, x, "weight")
+    _vec(bias, x, "bias", 3 * C)
+    o = _out_like(out, x)
+    st = load().vinf_projected_dual_domain_attn(_ptr(x), _ptr(weight), _ptr(bias), _ptr(o), F, H, W, C, head_dim,
+                                                16, 16, float(scale), _dtype_code(x), _stream(x.device, stream))
+    _check("vinf_projected_dual_domain_attn", st)
+    return o
 
 
 def _workspace(x: torch.Tensor, groups: int, workspace):

@@ -385,6 +385,29 @@ vinf_status vinf_dual_domain_attn(const void* q, const void* k, const void* v, v
                       (hipStream_t)stream);
 }
 
+vinf_status vinf_projected_dual_domain_attn(const void* x, const void* weight, const float* bias, void* o, int F,
+                                            int H, int W, int C, int head_dim, int n_local, int n_global, float scale,
+                                            vinf_dtype dt, vinf_stream stream) {
+    const char* fn = "vinf_projected_dual_domain_attn";
+    size_t bytes;
+    VINF_TRY(check_shape(fn, F, H, W, C, dt, &bytes));
+    VINF_TRY(check_tensor(fn, "x", x, true));
+    VINF_TRY(check_tensor(fn, "weight", weight, true));
+    VINF_TRY(check_tensor(fn, "o", o, true));
+    VINF_TRY(check_f32(fn, "bias", bias));
+    VINF_TRY(check_dda_heads(fn, C, head_dim, n_local, n_global, scale));
+    if (dt != VINF_BF16)
+        return fail(VINF_ERR_UNSUPPORTED, "%s: bf16 only (float32: vinf_qkv_project, then vinf_dual_domain_attn)", fn);
+    if (n_local != 16 || n_global != 16)
+        return fail(VINF_ERR_UNSUPPORTED, "%s: the full key set only (n_local = n_global = 16), got %d and %d", fn,
+                    n_local, n_global);
+    const size_t wbytes = (size_t)3 * C * C * 2;
+    if (overlap(o, bytes, x, bytes) || overlap(o, bytes, weight, wbytes) || overlap(o, bytes, bias, (size_t)3 * C * 4))
+        return fail(VINF_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+    if (scale <= 0.f) scale = 0.125f;  // 1/sqrt(64)
+    return launch_dda_projected(x, weight, bias, o, F, H * W, C, scale, (hipStream_t)stream);
+}
+
 vinf_status vinf_dda_clip_halo(int F_total, int f0, int Fc, int n_local, int* n_pre, int* n_post) {
     const char* fn = "vinf_dda_clip_halo";
     if (!n_pre || !n_post) return fail(VINF_ERR_INVALID_ARG, "%s: NULL output", fn);

@@ -99,6 +99,12 @@ vinf_status launch_conv3_gn(const void* x, const void* ctx_pre, const void* ctx_
 vinf_status launch_qkv_project(const void* x, const void* w, const float* bias, void* q, void* k, void* v, int F,
                                int S, int C, vinf_dtype dt, hipStream_t st);
 
+// Attention over the projected tokens of x (bf16): the Q/K/V maps of
+// weight [3][C][C] (+ bias [3][C] or null) computed per work item, never
+// written out; the full key set (16 local + 16 global).
+vinf_status launch_dda_projected(const void* x, const void* w, const float* bias, void* o, int F, int S, int C,
+                                 float scale, hipStream_t st);
+
 // Attention of query frames f0 .. f0+nq-1 of an F-frame video; k/v hold
 // frames kf0 .. kend-1; kg/vg the global rows or null (read from k/v).
 vinf_status launch_dda(const void* q, const void* k, const void* v, const void* kg, const void* vg, void* o,

@@ -53,6 +53,8 @@
 //     registers), the other computes from its own buffer; a workgroup barrier
 //     ends each phase.  HBM traffic and the VALU-bound compute overlap
 //     instead of alternating.
+// Projected kernel (dda_proj_bf16): the Q/K/V projection inside the
+// attention's work items (see its comment below).
 // fp32 kernel (dda_f32): one query per thread, fp32 FMA, keys read through
 // the cache; used for float32 I/O.
 #include <math.h>
@@ -463,6 +465,255 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     }
 }
 
+// ---- Q/K/V projection fused with the attention ----
+//
+// The query token comes from frame t, and the keys and values are computed
+// from the tokens of its frame set (dual-domain attention paragraph): here
+// q, k and v are three C x C linear maps of the input tokens (the reading of
+// vinf_qkv_project), computed inside the attention's work item so they never
+// reach HBM.  Per item (one location, one head, 256 query frames), one
+// 256-thread workgroup:
+//   1. projects the item's rows of x, the <= 271 frames its local windows
+//      cover and the 16 global frames, onto the head's 64 q, 64 k and 64 v
+//      channels: a 288 x 192 x C product on v_mfma_f32_16x16x32_bf16, the
+//      weight fragment as the A operand and the accumulators started from the
+//      bias, with the same K order as vinf_qkv_project's kernel, so every
+//      value rounds to the same bf16;
+//   2. writes the results straight into the attention's LDS layout: K rows,
+//      V frame pairs, the global rows, and the q rows in the freed staging
+//      area;
+//   3. runs the attention's compute on them (dda_compute).
+// x and weight slices (32 channels) are staged through registers, their
+// loads issued two slices ahead, double buffered in LDS with one barrier per
+// slice; 4 waves, each 9 row tiles x 6 column tiles (216 accumulators).
+constexpr int PJ_ROWS = 288;                            // 18 row tiles: <= 271 local + 16 global
+constexpr int PJ_COLS = 3 * DDA_D;                      // 12 column tiles: q, k, v of the head
+constexpr int PJ_XS = PJ_ROWS * 64;                     // one 32-channel slice of the rows
+constexpr int PJ_WS = PJ_COLS * 64;                     // one 32-channel slice of the weight rows
+constexpr int PJ_STAGE = PJ_XS + PJ_WS;
+constexpr int PJ_LDS = DDA_LDS_BYTES + 2 * PJ_STAGE;    // the attention slice, then two stages (or the q rows)
+static_assert(DDA_TQ * 128 <= 2 * PJ_STAGE, "the q rows fit in the staging area");
+static_assert(PJ_LDS <= 160 * 1024, "LDS of one CU");
+static_assert(DdaFull::KROWS + DDA_G <= PJ_ROWS, "the projected rows");
+constexpr int PJ_XT = (PJ_ROWS * 4 + 255) / 256;        // x chunks per thread and slice
+constexpr int PJ_WT = PJ_COLS * 4 / 256;                // weight chunks per thread and slice
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+dda_proj_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+              uint16_t* __restrict__ o, DdaGeo g) {
+    __shared__ __attribute__((aligned(16))) char lds[PJ_LDS];
+    using SL = DdaFull;
+    const int heads = g.C / DDA_D;
+    const int64_t rs = (int64_t)g.S * g.C;
+    const int lt = threadIdx.x, lane = lt & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(lt >> 6);
+    const int wm = wv & 1, wn = wv >> 1;            // row tiles 9wm .. 9wm+8, column tiles 6wn .. 6wn+5
+    // Persistent: workgroup b runs on XCD b % 8 (the dispatcher deals them
+    // round-robin), and the eight XCDs take contiguous eighths of the item
+    // list, so the items running at once on an XCD are neighbours: the heads
+    // of one location, which read the same rows of x, share that XCD's L2.
+    const int G = gridDim.x, b = blockIdx.x;
+    const int per_xcd = (g.nitems + 7) / 8;
+    auto item_of = [&](int k) -> int {
+        if (G & 7) {
+            const int i = b + k * G;
+            return i < g.nitems ? i : -1;
+        }
+        const int kk = (b >> 3) + k * (G >> 3);
+        const int i = (b & 7) * per_xcd + kk;
+        return kk < per_xcd && i < g.nitems ? i : -1;
+    };
+    // x and the weight as buffers: byte offsets are 32-bit (the launcher
+    // rejects an x of 4 GiB or more)
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), (short)0, (int)0xffffffffu, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(w), (short)0, (int)0xffffffffu, 0x00020000);
+    for (int k = 0;; ++k) {
+        const int idx = item_of(k);
+        if (idx < 0) break;
+        const DdaItem it{idx % g.nstrips, (idx / g.nstrips) * DDA_TQ};
+        const int s = it.strip / heads, h = it.strip % heads;
+        const int F = g.F;
+        const int lo = dda_start(it.t0, F);
+        const int tlast = min(it.t0 + DDA_TQ, F) - 1;
+        const int nkr = dda_start(tlast, F) + DDA_L - lo;  // local rows: frames lo .. lo+nkr-1
+        const int plo = lo & ~1;
+        char* const stage = lds + DDA_LDS_BYTES;
+        // frame of projected row r: a local frame, a global frame, or none (-1)
+        auto frame_of = [&](int r) -> int {
+            if (r < nkr) return lo + r;
+            if (r < nkr + DDA_G) return (int)(((int64_t)(r - nkr) * F) / DDA_G);
+            return -1;
+        };
+
+        // The V pair rows are filled half by half below; a half with no projected
+        // frame (before lo, past the last) carries weight 0 and must read as 0.
+        for (int i = lt; i < (DDA_G / 2) * 256 / 16; i += 256)
+            *reinterpret_cast<u32x4_t*>(lds + SL::VG + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = lt; i < SL::VPAIRS * DDA_VSTR / 16; i += 256)
+            *reinterpret_cast<u32x4_t*>(lds + SL::VP + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
+
+        // accumulators: row tile 9wm + mi, column tile 6wn + ni; lane l holds
+        // columns 4 (l / 16) .. +3 of the tile's row l % 16, started from the bias
+        const int lr = lane & 15, lc = lane >> 4;
+        f32x4_t acc[9][6];
+#pragma unroll
+        for (int ni = 0; ni < 6; ++ni) {
+            const int c0 = (6 * wn + ni) * 16 + 4 * lc, p = c0 / DDA_D;
+            f32x4_t b = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (bias) {
+                const float* bp = bias + p * g.C + h * DDA_D + (c0 % DDA_D);
+                b = f32x4_t{bp[0], bp[1], bp[2], bp[3]};
+            }
+#pragma unroll
+            for (int mi = 0; mi < 9; ++mi) acc[mi][ni] = b;
+        }
+        // Staging of slice kc: thread task i -> row i / 4, 16-byte chunk i % 4, at
+        // LDS slot chunk ^ ((row >> 1) & 3) of the row's 64 bytes, so that the
+        // fragment reads (16 rows, one chunk per lane group) are conflict-free.
+        // Each thread's chunk offsets are formed once per item; a slice is the
+        // buffer loads' scalar offset.  Every lane loads (rows without a frame
+        // read frame 0, and their value is dropped when written), so the loads
+        // are straight-line code and each wait before the writes counts only
+        // the older register stage's loads.
+        uint32_t xo[PJ_XT], wo[PJ_WT], xin = 0;
+#pragma unroll
+        for (int j = 0; j < PJ_XT; ++j) {
+            const int task = lt + 256 * j;
+            const int f = frame_of(task >> 2);
+            const bool ok = f >= 0 && f < F;
+            xo[j] = (uint32_t)((((int64_t)(ok ? f : 0) * g.S + s) * g.C + (task & 3) * 8) * 2);
+            xin |= (ok ? 1u : 0u) << j;
+        }
+#pragma unroll
+        for (int j = 0; j < PJ_WT; ++j) {
+            const int task = lt + 256 * j;
+            const int n = task >> 2, p = n / DDA_D;   // column n: output p (q, k, v), channel n % 64 of the head
+            wo[j] = (uint32_t)((((int64_t)p * g.C + h * DDA_D + (n % DDA_D)) * g.C + (task & 3) * 8) * 2);
+        }
+        auto load = [&](int kc, u32x4_t (&xr)[PJ_XT], u32x4_t (&wr)[PJ_WT]) {
+#pragma unroll
+            for (int j = 0; j < PJ_XT; ++j) xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo[j], kc * 64, 0);
+#pragma unroll
+            for (int j = 0; j < PJ_WT; ++j) wr[j] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wo[j], kc * 64, 0);
+        };
+        auto put = [&](int b, const u32x4_t (&xr)[PJ_XT], const u32x4_t (&wr)[PJ_WT]) {
+            char* xs = stage + b * PJ_STAGE;
+            char* ws = xs + PJ_XS;
+#pragma unroll
+            for (int j = 0; j < PJ_XT; ++j) {
+                const int task = lt + 256 * j;
+                if (task < PJ_ROWS * 4) {
+                    const int r = task >> 2, c = task & 3;
+                    const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4_t*>(xs + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)) = (xin >> j) & 1u ? xr[j] : z;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PJ_WT; ++j) {
+                const int task = lt + 256 * j;
+                const int r = task >> 2, c = task & 3;
+                *reinterpret_cast<u32x4_t*>(ws + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)) = wr[j];
+            }
+        };
+        const int rd_off = lr * 64 + ((lc ^ ((lr >> 1) & 3)) << 4);
+        const int nk = g.C / 32;  // even (C % 64 == 0)
+        // Two register stages: slice kc: issue slice kc+2's loads (into stage kc &
+        // 1, free since slice kc went to LDS; the last two slices reload slice
+        // nk-1, unused, so there is no branch around the loads), multiply from LDS
+        // buffer kc & 1, write slice kc+1 (loaded a slice ago) to the other
+        // buffer, barrier.
+        u32x4_t xr[2][PJ_XT], wr[2][PJ_WT];
+        auto step = [&](int kc, auto par) {
+            constexpr int P = decltype(par)::value;
+            load(min(kc + 2, nk - 1), xr[P], wr[P]);
+            const char* xs = stage + P * PJ_STAGE;
+            const char* ws = xs + PJ_XS;
+            bf16x8_t xf[9], wf[6];
+#pragma unroll
+            for (int mi = 0; mi < 9; ++mi) xf[mi] = *reinterpret_cast<const bf16x8_t*>(xs + (9 * wm + mi) * 16 * 64 + rd_off);
+#pragma unroll
+            for (int ni = 0; ni < 6; ++ni) wf[ni] = *reinterpret_cast<const bf16x8_t*>(ws + (6 * wn + ni) * 16 * 64 + rd_off);
+#pragma unroll
+            for (int ni = 0; ni < 6; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < 9; ++mi)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ni], xf[mi], acc[mi][ni], 0, 0, 0);
+            if (kc + 1 < nk) put(1 - P, xr[1 - P], wr[1 - P]);
+            __syncthreads();
+        };
+        load(0, xr[0], wr[0]);
+        load(min(1, nk - 1), xr[1], wr[1]);
+        put(0, xr[0], wr[0]);
+        __syncthreads();
+        for (int kc = 0; kc < nk; kc += 2) {
+            step(kc, std::integral_constant<int, 0>{});
+            step(kc + 1, std::integral_constant<int, 1>{});
+        }
+
+        // Results into the attention's layout (the staging area is free now: the
+        // loop ended with a barrier, which also ordered the zero fill above).
+        // Frames outside the video become zeros, as the unfused attention reads
+        // them.
+        char* const qrows = stage;
+#pragma unroll
+        for (int mi = 0; mi < 9; ++mi) {
+            const int r = (9 * wm + mi) * 16 + lr;
+            const int f = frame_of(r);
+            const bool in = f >= 0 && f < F;
+#pragma unroll
+            for (int ni = 0; ni < 6; ++ni) {
+                const int c0 = (6 * wn + ni) * 16 + 4 * lc, p = c0 / DDA_D, j0 = c0 % DDA_D;
+                const f32x4_t a = acc[mi][ni];
+                const uint32_t u0 = in ? pack_bf16x2(a[0], a[1]) : 0u, u1 = in ? pack_bf16x2(a[2], a[3]) : 0u;
+                if (r < nkr) {
+                    if (p == 0) {
+                        if (in && f >= it.t0 && f < it.t0 + DDA_TQ)
+                            *reinterpret_cast<uint2*>(qrows + (f - it.t0) * 128 + j0 * 2) = uint2{u0, u1};
+                    } else if (p == 1) {
+                        *reinterpret_cast<uint2*>(lds + SL::KL + r * DDA_KSTR + j0 * 2) = uint2{u0, u1};
+                    } else {
+                        char* vp = lds + SL::VP + ((f - plo) >> 1) * DDA_VSTR + j0 * 4 + ((f - plo) & 1) * 2;
+                        *reinterpret_cast<uint16_t*>(vp) = (uint16_t)u0;
+                        *reinterpret_cast<uint16_t*>(vp + 4) = (uint16_t)(u0 >> 16);
+                        *reinterpret_cast<uint16_t*>(vp + 8) = (uint16_t)u1;
+                        *reinterpret_cast<uint16_t*>(vp + 12) = (uint16_t)(u1 >> 16);
+                    }
+                } else if (r < nkr + DDA_G) {
+                    const int i = r - nkr;
+                    if (p == 1) {
+                        *reinterpret_cast<uint2*>(lds + SL::KG + i * 128 + j0 * 2) = uint2{u0, u1};
+                    } else if (p == 2) {
+                        char* vp = lds + SL::VG + (i >> 1) * 256 + j0 * 4 + (i & 1) * 2;
+                        *reinterpret_cast<uint16_t*>(vp) = (uint16_t)u0;
+                        *reinterpret_cast<uint16_t*>(vp + 4) = (uint16_t)(u0 >> 16);
+                        *reinterpret_cast<uint16_t*>(vp + 8) = (uint16_t)u1;
+                        *reinterpret_cast<uint16_t*>(vp + 12) = (uint16_t)(u1 >> 16);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        uint32_t qv[32];
+        if (it.t0 + lt < F) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const u32x4_t u = *reinterpret_cast<const u32x4_t*>(qrows + lt * 128 + c * 16);
+                qv[4 * c] = u[0];
+                qv[4 * c + 1] = u[1];
+                qv[4 * c + 2] = u[2];
+                qv[4 * c + 3] = u[3];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 32; ++c) qv[c] = 0u;  // a lane past the last query computes a throw-away copy
+        }
+        dda_compute<DDA_L, DDA_G, DDA_TQ>(lds, o, g, rs, heads, it, lt, qv);
+        __syncthreads();  // the next item's zero fill and staging overwrite this item's LDS
+    }
+}
+
 // float32 I/O: one query per thread, keys read through the cache.
 // n_local, n_global: 16 or 0.
 __global__ void __launch_bounds__(64) dda_f32(const float* __restrict__ q, const float* __restrict__ k,
@@ -515,6 +766,39 @@ __global__ void __launch_bounds__(64) dda_f32(const float* __restrict__ q, const
 
 namespace vinf_host {
 using namespace vinf;
+
+vinf_status launch_dda_projected(const void* x, const void* w, const float* bias, void* o, int F, int S, int C,
+                                 float scale, hipStream_t st) {
+    const int heads = C / DDA_D;
+    DdaGeo g;
+    g.kg = g.vg = nullptr;
+    g.F = F;
+    g.f0 = 0;
+    g.nq = F;
+    g.kf0 = 0;
+    g.kend = F;
+    g.S = S;
+    g.C = C;
+    g.sl2e = scale * 1.4426950408889634f;
+    const int64_t nstrips = (int64_t)S * heads, nchunks = (F + DDA_TQ - 1) / DDA_TQ;
+    if (nstrips * nchunks > 0x7fffffff)
+        return fail(VINF_ERR_UNSUPPORTED, "projected_dual_domain_attn: more than 2^31 work items");
+    g.nstrips = (int)nstrips;
+    g.nchunks = (int)nchunks;
+    g.nfull = g.nitems = (int)(nstrips * nchunks);
+    if ((uint64_t)F * S * C * 2 > 0xffffffffull)
+        return fail(VINF_ERR_UNSUPPORTED, "projected_dual_domain_attn: x of 4 GiB or more (32-bit buffer offsets)");
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(VINF_ERR_HIP, "projected_dual_domain_attn: cannot query the device");
+    // one persistent workgroup per CU, a multiple of 8 of them when there are
+    // enough items (the kernel's XCD-contiguous item order needs it)
+    int grid = (int)std::min<int64_t>(cus, g.nitems);
+    if (grid >= 8) grid &= ~7;
+    hipLaunchKernelGGL(dda_proj_bf16, dim3((uint32_t)grid), dim3(256), 0, st, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w), bias, static_cast<uint16_t*>(o), g);
+    return check_launch("projected_dual_domain_attn");
+}
 
 vinf_status launch_dda(const void* q, const void* k, const void* v, const void* kg, const void* vg, void* o,
                        int F, int f0, int nq, int kf0, int kend, int S, int C, int n_local, int n_global,
