@@ -138,6 +138,8 @@ def test_projected_attention_at_workload_size():
     (5, 2, 2, 64, True),       # F < 16: every frame is local context, rows past F are zeros
     (16, 3, 3, 192, False),    # F = 16: one window, global frames 0 .. 15
     (40, 4, 5, 640, True),     # ten heads
+    (23, 2, 3, 1280, False),   # twenty heads, 40 slices of 32 channels
+    (1, 3, 2, 128, True),      # one frame: its window and every global row are frame 0
 ])
 def test_fused_projected_attention(F, H, W, C, bias):
     announce(f"fused projected attention F={F} H={H} W={W} C={C} bias={bias}")
