@@ -126,16 +126,35 @@ struct DdaItem {
     int strip, t0;
 };
 
+// V rows f, f+1 (16 bytes each, 8 dims) -> two 16-byte pair chunks
+// (v[f][d], v[f+1][d]) in LDS at dst.
+__device__ __forceinline__ void dda_put_pairs(char* dst, const u32x4_t& a, const u32x4_t& b) {
+    const u32x4_t w0 = {perm_lo(a[0], b[0]), perm_hi(a[0], b[0]), perm_lo(a[1], b[1]), perm_hi(a[1], b[1])};
+    const u32x4_t w1 = {perm_lo(a[2], b[2]), perm_hi(a[2], b[2]), perm_lo(a[3], b[3]), perm_hi(a[3], b[3])};
+    *reinterpret_cast<u32x4_t*>(dst) = w0;
+    *reinterpret_cast<u32x4_t*>(dst + 16) = w1;
+}
+
 // Stage one strip's rows for queries t0 .. t0+R-1 into its slice `buf`
 // (NT threads, lt = 0..NT-1) and load the q row of query t0 + lt into qv.
-// NL / NG: local / global keys present (16 or 0).
+// NL / NG: local / global keys present (16 or 0).  A thread moves 16-byte
+// chunks: chunk lt&7 of local K rows lt>>3 + (NT/8)*i, the same of V pair
+// rows, and global-row tasks lt + NT*n.  A full item (R = 256) issues every
+// load before its first LDS write, so its stage costs one memory round trip;
+// the smaller remainder slices write each row kind before loading the next
+// (fewer registers live at once).
 template <int NL, int NG, int R, int NT>
 __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t* __restrict__ q,
                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                           const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
                                           uint32_t (&qv)[32]) {
     using SL = DdaSlice<R>;
+    constexpr bool ALL_FIRST = R == DDA_TQ;
     constexpr int RSTEP = NT / 8;  // rows one pass of the threads covers (8 chunks per row)
+    constexpr int NIK = NL > 0 ? (SL::KROWS + RSTEP - 1) / RSTEP : 1;
+    constexpr int NIV = NL > 0 ? (SL::VPAIRS + RSTEP - 1) / RSTEP : 1;
+    constexpr int NGTASK = DDA_G * 8 + (DDA_G / 2) * 8;  // global K row chunks, then V pair chunks
+    constexpr int NGT = NG > 0 ? (NGTASK + NT - 1) / NT : 1;
     const int s = it.strip / heads, h = it.strip % heads;
     const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int t = it.t0 + lt;
@@ -153,90 +172,112 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
 #pragma unroll
         for (int c = 0; c < 32; ++c) qv[c] = 0u;  // a lane past the last query computes a throw-away copy
     }
+    const int c8 = lt & 7, r0 = lt >> 3;
+    // Frames outside [kf0, kend) are not in k/v: their rows are zero-filled
+    // (only frames past the video's last frame, or the unused half of a pair
+    // row, which carry no weight, fall outside).
+    int nkr = 0, np = 0;
+    u32x4_t ku[NIK], va[NIV], vb[NIV];
+    auto store_k = [&]() {
+        char* dst = buf + SL::KL + r0 * DDA_KSTR + c8 * 16;
+#pragma unroll
+        for (int i = 0; i < NIK; ++i)
+            if (r0 + RSTEP * i < nkr) *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_KSTR) = ku[i];
+    };
+    auto store_v = [&]() {
+        char* dst = buf + SL::VP + r0 * DDA_VSTR + c8 * 32;
+#pragma unroll
+        for (int i = 0; i < NIV; ++i)
+            if (r0 + RSTEP * i < np) dda_put_pairs(dst + RSTEP * i * DDA_VSTR, va[i], vb[i]);
+    };
     if constexpr (NL > 0) {
         const int tlast = min(it.t0 + R, g.f0 + g.nq) - 1;
         const int lo = dda_start(it.t0, g.F);
         const int stl = dda_start(tlast, g.F);
-        const int nkr = stl + DDA_L - lo;             // K rows [lo, lo+nkr), <= R + 15
+        nkr = stl + DDA_L - lo;                       // K rows [lo, lo+nkr), <= R + 15
         const int plo = lo & ~1;
-        const int np = (stl + DDA_L + 2 - plo) >> 1;  // V pairs cover [plo, plo+2np), <= (R + 18) / 2
-        // Frames outside [kf0, kend) are not in k/v: their rows are zero-filled
-        // (only frames past the video's last frame, or the unused half of a
-        // pair row, which carry no weight, fall outside).
-        // local K rows: this thread's chunk c = lt&7 of rows lt>>3 + RSTEP*i
-        {
-            constexpr int NI = (SL::KROWS + RSTEP - 1) / RSTEP;
-            const int c = lt & 7, r0 = lt >> 3;
-            const uint16_t* src = k + col + (int64_t)(lo + r0 - g.kf0) * rs + c * 8;
-            char* dst = buf + SL::KL + r0 * DDA_KSTR + c * 16;
-            u32x4_t u[NI];
+        np = (stl + DDA_L + 2 - plo) >> 1;            // V pairs cover [plo, plo+2np), <= (R + 18) / 2
+        const uint16_t* ks = k + col + (int64_t)(lo + r0 - g.kf0) * rs + c8 * 8;
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int r = r0 + RSTEP * i;
-                u[i] = u32x4_t{0u, 0u, 0u, 0u};
-                if (r < nkr && lo + r < g.kend)
-                    u[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(RSTEP * i) * rs);
-            }
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-                if (r0 + RSTEP * i < nkr) *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_KSTR) = u[i];
+        for (int i = 0; i < NIK; ++i) {
+            const int r = r0 + RSTEP * i;
+            ku[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (r < nkr && lo + r < g.kend) ku[i] = *reinterpret_cast<const u32x4_t*>(ks + (int64_t)(RSTEP * i) * rs);
         }
-        // local V as frame pairs: this thread's 8-dim group oc = lt&7 of pairs lt>>3 + RSTEP*i
-        {
-            constexpr int NI = (SL::VPAIRS + RSTEP - 1) / RSTEP;
-            const int oc = lt & 7, p0 = lt >> 3;
-            const uint16_t* src = v + col + (int64_t)(plo + 2 * p0 - g.kf0) * rs + oc * 8;
-            char* dst = buf + SL::VP + p0 * DDA_VSTR + oc * 32;
-            u32x4_t a[NI], b[NI];
+        if constexpr (!ALL_FIRST) store_k();
+        const uint16_t* vs = v + col + (int64_t)(plo + 2 * r0 - g.kf0) * rs + c8 * 8;
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int p = p0 + RSTEP * i, fa = plo + 2 * p;
-                a[i] = u32x4_t{0u, 0u, 0u, 0u};
-                b[i] = u32x4_t{0u, 0u, 0u, 0u};
-                if (p < np && fa >= g.kf0 && fa < g.kend)
-                    a[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(2 * RSTEP * i) * rs);
-                if (p < np && fa + 1 < g.kend)
-                    b[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(2 * RSTEP * i + 1) * rs);
-            }
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                if (p0 + RSTEP * i < np) {
-                    u32x4_t w0 = {perm_lo(a[i][0], b[i][0]), perm_hi(a[i][0], b[i][0]), perm_lo(a[i][1], b[i][1]),
-                                  perm_hi(a[i][1], b[i][1])};
-                    u32x4_t w1 = {perm_lo(a[i][2], b[i][2]), perm_hi(a[i][2], b[i][2]), perm_lo(a[i][3], b[i][3]),
-                                  perm_hi(a[i][3], b[i][3])};
-                    *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_VSTR) = w0;
-                    *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_VSTR + 16) = w1;
-                }
-            }
+        for (int i = 0; i < NIV; ++i) {
+            const int p = r0 + RSTEP * i, fa = plo + 2 * p;
+            va[i] = u32x4_t{0u, 0u, 0u, 0u};
+            vb[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (p < np && fa >= g.kf0 && fa < g.kend)
+                va[i] = *reinterpret_cast<const u32x4_t*>(vs + (int64_t)(2 * RSTEP * i) * rs);
+            if (p < np && fa + 1 < g.kend)
+                vb[i] = *reinterpret_cast<const u32x4_t*>(vs + (int64_t)(2 * RSTEP * i + 1) * rs);
         }
+        if constexpr (!ALL_FIRST) store_v();
     }
     if constexpr (NG > 0) {
-        // 192 tasks: global K row chunks (tasks 0..127) and V pair chunks (128..191)
         const uint16_t* kgb = g.kg ? static_cast<const uint16_t*>(g.kg) : k;
         const uint16_t* vgb = g.vg ? static_cast<const uint16_t*>(g.vg) : v;
         auto grow = [&](int i) -> int64_t {  // row of global frame i in kgb / vgb
             return g.kg ? (int64_t)i : (int64_t)(((int64_t)i * g.F) / DDA_G) - g.kf0;
         };
+        u32x4_t ga[NGT], gb[NGT];
 #pragma unroll
-        for (int task = lt; task < DDA_G * 8 + (DDA_G / 2) * 8; task += NT) {
+        for (int n = 0; n < NGT; ++n) {
+            const int task = lt + NT * n;
             if (task < DDA_G * 8) {
-                const int i = task >> 3, c = task & 7;
-                *reinterpret_cast<u32x4_t*>(buf + SL::KG + i * 128 + c * 16) =
-                    *reinterpret_cast<const u32x4_t*>(kgb + col + grow(i) * rs + c * 8);
-            } else {
-                const int j = task - DDA_G * 8;
-                const int p = j >> 3, oc = j & 7;
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p) * rs + oc * 8);
-                const u32x4_t b = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p + 1) * rs + oc * 8);
-                u32x4_t w0 = {perm_lo(a[0], b[0]), perm_hi(a[0], b[0]), perm_lo(a[1], b[1]), perm_hi(a[1], b[1])};
-                u32x4_t w1 = {perm_lo(a[2], b[2]), perm_hi(a[2], b[2]), perm_lo(a[3], b[3]), perm_hi(a[3], b[3])};
-                char* dst = buf + SL::VG + p * 256 + oc * 32;
-                *reinterpret_cast<u32x4_t*>(dst) = w0;
-                *reinterpret_cast<u32x4_t*>(dst + 16) = w1;
+                ga[n] = *reinterpret_cast<const u32x4_t*>(kgb + col + grow(task >> 3) * rs + (task & 7) * 8);
+            } else if (task < NGTASK) {
+                const int p = (task - DDA_G * 8) >> 3, oc = task & 7;
+                ga[n] = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p) * rs + oc * 8);
+                gb[n] = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p + 1) * rs + oc * 8);
             }
         }
+        if constexpr (ALL_FIRST && NL > 0) {
+            store_k();
+            store_v();
+        }
+#pragma unroll
+        for (int n = 0; n < NGT; ++n) {
+            const int task = lt + NT * n;
+            if (task < DDA_G * 8)
+                *reinterpret_cast<u32x4_t*>(buf + SL::KG + (task >> 3) * 128 + (task & 7) * 16) = ga[n];
+            else if (task < NGTASK)
+                dda_put_pairs(buf + SL::VG + ((task - DDA_G * 8) >> 3) * 256 + (task & 7) * 32, ga[n], gb[n]);
+        }
+    } else if constexpr (ALL_FIRST && NL > 0) {
+        store_k();
+        store_v();
     }
+}
+
+// a.x*b.x + a.y*b.y for bf16 pairs, fp32 (the three-operand v_dot2_f32_bf16
+// with a zero addend: a chain starts without a zeroed accumulator).
+__device__ __forceinline__ float dot2_zero(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Wait until at most n LDS reads of this wave are outstanding (s_waitcnt
+// lgkmcnt(n), n <= 15).  The scheduling barriers keep the reads issued before
+// it above it and the dot products after it below it.
+__device__ __forceinline__ void lds_wait(int n) {
+    __builtin_amdgcn_sched_barrier(0);
+    switch (n) {
+#define VINF_LGKM_CASE(k) \
+    case k: __builtin_amdgcn_s_waitcnt(0xC07F | ((k) << 8)); break;
+        VINF_LGKM_CASE(0) VINF_LGKM_CASE(1) VINF_LGKM_CASE(2) VINF_LGKM_CASE(3)
+        VINF_LGKM_CASE(4) VINF_LGKM_CASE(5) VINF_LGKM_CASE(6) VINF_LGKM_CASE(7)
+        VINF_LGKM_CASE(8) VINF_LGKM_CASE(9) VINF_LGKM_CASE(10) VINF_LGKM_CASE(11)
+        VINF_LGKM_CASE(12) VINF_LGKM_CASE(13) VINF_LGKM_CASE(14) VINF_LGKM_CASE(15)
+#undef VINF_LGKM_CASE
+        default: __builtin_amdgcn_s_waitcnt(0xC07F | (15 << 8)); break;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Compute query t0 + lt of a strip staged in slice `buf` (layout DdaSlice<R>).
@@ -262,7 +303,8 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     const int st = dda_start(t, F);
 
     // ---- scores: one K row (8 x 16 B) per key; the next row's reads are
-    // issued before the current row's dot products ----
+    // issued before the current row's dot products, and one wait per row
+    // covers all eight (a wait per 16-byte read costs an issue slot each) ----
     float sc[NK];
     const char* krow = buf + SL::KL + (st - lo) * DDA_KSTR;
     auto key_row = [&](int i) -> const char* {
@@ -277,11 +319,12 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 #pragma unroll
             for (int c = 0; c < 8; ++c) kb[(i + 1) & 1][c] = *reinterpret_cast<const u32x4_t*>(key_row(i + 1) + c * 16);
         }
-        float a = 0.f;
+        lds_wait(i + 1 < NK ? 8 : 0);  // row i has landed; row i+1's 8 reads may be in flight
+        float a = dot2_zero(qv[0], kb[i & 1][0][0]);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const u32x4_t u = kb[i & 1][c];
-            a = dot2_bf16(qv[4 * c], u[0], a);
+            if (c > 0) a = dot2_bf16(qv[4 * c], u[0], a);
             a = dot2_bf16(qv[4 * c + 1], u[1], a);
             a = dot2_bf16(qv[4 * c + 2], u[2], a);
             a = dot2_bf16(qv[4 * c + 3], u[3], a);
@@ -290,14 +333,16 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     }
 
     // ---- lane-local softmax (base 2, scale folded in) ----
+    // (the maximum is taken before the scaling: sl2e > 0 keeps the order)
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-        sc[j] = (j < NL && j >= nl) ? -INFINITY : sc[j] * g.sl2e;
+        sc[j] = (j < NL && j >= nl) ? -INFINITY : sc[j];
         m = fmaxf(m, sc[j]);
     }
+    const float msl = -(m * g.sl2e);
 #pragma unroll
-    for (int j = 0; j < NK; ++j) sc[j] = __builtin_amdgcn_exp2f(sc[j] - m);
+    for (int j = 0; j < NK; ++j) sc[j] = __builtin_amdgcn_exp2f(fmaf(sc[j], g.sl2e, msl));
 
     // weights as bf16 pairs matching the V pair rows: NLP local, then 8 global
     uint32_t w[NP];
@@ -323,15 +368,13 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 
     // ---- weighted sum of V over the NP pair rows, next row's reads issued
     // before the current row's dot products ----
-    float acc[DDA_D];
-#pragma unroll
-    for (int d = 0; d < DDA_D; ++d) acc[d] = 0.f;
+    float acc[DDA_D];  // set by pair row 0
     const char* vrow = buf + SL::VP + ((st - plo) >> 1) * DDA_VSTR;
     auto val_row = [&](int j) -> const char* {
         return j < NLP ? vrow + j * DDA_VSTR : buf + SL::VG + (j - NLP) * 256;
     };
     // half rows (32 dims, 8 x 16 B) double-buffered: step 2j + hh reads
-    // dims 32*hh.. of pair row j
+    // dims 32*hh.. of pair row j; one wait per step
     u32x4_t vb[2][8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) vb[0][c] = *reinterpret_cast<const u32x4_t*>(val_row(0) + c * 16);
@@ -344,12 +387,15 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
             for (int c = 0; c < 8; ++c)
                 vb[(step + 1) & 1][c] = *reinterpret_cast<const u32x4_t*>(val_row(jn) + hn * 128 + c * 16);
         }
+        lds_wait(step + 1 < 2 * NP ? 8 : 0);
         const uint32_t wj = w[j];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[32 * hh + 4 * c + e] = dot2_bf16(wj, vb[step & 1][c][e], acc[32 * hh + 4 * c + e]);
+            for (int e = 0; e < 4; ++e) {
+                float& r = acc[32 * hh + 4 * c + e];
+                r = j == 0 ? dot2_zero(wj, vb[step & 1][c][e]) : dot2_bf16(wj, vb[step & 1][c][e], r);
+            }
         }
     }
 

@@ -103,9 +103,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t cv_rsrc(const void* base, uint
 // TAPS = 3: the temporal conv (tap k multiplies frame f+k-1, one output y).
 // TAPS = 1: the Q/K/V projection, the same GEMM with no frame shift: N spans
 // the 3*C rows of the [3][C][C] weight, and output channel n goes to
-// y, y1 or y2 (Q, K, V) by n / C.  Tiles of one location block are
-// consecutive, so a workgroup stages each x tile from L2 for the second and
-// third output.  With one tap a slice holds a third of the conv's MFMAs, so
+// y, y1 or y2 (Q, K, V) by n / C.  The tiles of one location block run at
+// the same time on three workgroups of one XCD, so two of the three stagings
+// of each x tile come from L2.  With one tap a slice holds a third of the conv's MFMAs, so
 // KS = 2 slices share a barrier (more work in flight per load latency).
 template <int NF, int WN, int TAPS, int KS, bool GN>
 __global__ void __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(WN, WN)))
@@ -131,9 +131,22 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
     const int lr = lane & 15, lc = lane >> 4;
     const int nk = C / CV_BK;
     const int ntiles = nfb * nlb * ntn;
-    // contiguous range of tiles per workgroup
-    const int t_begin = (int)(((int64_t)ntiles * blockIdx.x) / gridDim.x);
-    const int t_end = (int)(((int64_t)ntiles * (blockIdx.x + 1)) / gridDim.x);
+    // The workgroup's tiles: t_first, t_first + t_step, ... below t_stop.
+    // Conv: a contiguous range.  Projection (grid a multiple of 8): the tiles
+    // go to the 8 XCDs in 8 contiguous ranges, dealt round-robin to the
+    // workgroups of an XCD (hardware workgroup b runs on XCD b % 8), so the
+    // Q, K and V tiles of a location block run at the same time on one L2 and
+    // its x tile comes from HBM once.
+    int t_first = (int)(((int64_t)ntiles * blockIdx.x) / gridDim.x), t_step = 1;
+    int t_stop = (int)(((int64_t)ntiles * (blockIdx.x + 1)) / gridDim.x);
+    if (TAPS == 1 && (gridDim.x & 7) == 0) {
+        const int P = gridDim.x >> 3, xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int r0 = (int)(((int64_t)ntiles * xcd) >> 3), r1 = (int)(((int64_t)ntiles * (xcd + 1)) >> 3);
+        const int cnt = r1 - r0 > j ? (r1 - r0 - j + P - 1) / P : 0;
+        t_first = r0 + j;
+        t_step = P;
+        t_stop = t_first + cnt * P;
+    }
     const uint32_t frame_bytes = (uint32_t)S * (uint32_t)C * 2u;
     const __amdgpu_buffer_rsrc_t wr = cv_rsrc(w, 3u * (uint32_t)C * (uint32_t)C * 2u);
 
@@ -153,7 +166,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
 
     // Stage cursor: tile ti, slice ki of the next stage to issue, and ti's
     // coordinates (computed once per tile: tile_coords divides).
-    int ti = t_begin, ki = 0;
+    int ti = t_first, ki = 0;
     int cf0 = 0, cs0 = 0, cn0 = 0;
     auto cursor_tile = [&]() { tile_coords(ti, cf0, cs0, cn0); };
 
@@ -226,7 +239,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
             for (int mi = 0; mi < 4; ++mi) acc[mi][ni] = b;
         }
     };
-    if (t_begin < t_end) acc_init(t_begin);
+    if (t_first < t_stop) acc_init(t_first);
 
     // GroupNorm.  gn_ab is a table of channel pairs, 16 bytes each (a_2p,
     // a_2p+1, b_2p, b_2p+1), so a slice's coefficients are 256 contiguous
@@ -286,11 +299,11 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         ki += KS;
         if (ki >= nk) {
             ki = 0;
-            ++ti;
-            if (ti < t_end) cursor_tile();
+            ti += t_step;
+            if (ti < t_stop) cursor_tile();
         }
     };
-    if (t_begin < t_end) {
+    if (t_first < t_stop) {
         cursor_tile();
         issue_next(0);
         ab_issue(0, 0);    // stage 0
@@ -300,21 +313,21 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         if (tid < 4) reinterpret_cast<uint32_t*>(ab_lds + 512)[tid] = 0u;
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();                      // the coefficients of stages 0 and 1 and the zero slot
-        if (t_begin < t_end) {
+        if (t_first < t_stop) {
             int f0, s0, n0;
-            tile_coords(t_begin, f0, s0, n0);
+            tile_coords(t_first, f0, s0, n0);
             gn_blocks(f0, 0, 0, wv);
         }
     }
     int g = 0;  // stage counter across tiles (selects the buffer)
-    for (int t = t_begin; t < t_end; ++t) {
+    for (int t = t_first; t < t_stop; t += t_step) {
         for (int kc = 0; kc < nk; kc += KS, ++g) {
             // vmcnt(0): this wave's loads of stage g are in LDS (with GN, waited
             // for, and normalised, while stage g-1 was multiplied).
             if constexpr (!GN) __builtin_amdgcn_s_waitcnt(0x0f70);
             __syncthreads();                      // everyone's are; stage g-1 is no longer read
             const int f0_next = cf0;              // first frame of the tile of stage g+1, if there is one
-            if (ti < t_end) issue_next((g + 1) & 1);
+            if (ti < t_stop) issue_next((g + 1) & 1);
             ab_issue(ki, g & 1);                  // GN: the coefficients of stage g+2
             // GN: stage g+1 is normalised in the shadow of stage g's last MFMA
             // groups.  Each wave rewrites the frame blocks its own loads filled,
@@ -424,7 +437,7 @@ conv3_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ pre, con
         // stores and are first needed after the next stage's wait, so nothing
         // waits on them here (a load between stores would make its wait, on a
         // counter that also counts stores, wait for every store before it).
-        if (t + 1 < t_end) acc_init(t + 1);
+        if (t + t_step < t_stop) acc_init(t + t_step);
     }
 }
 
