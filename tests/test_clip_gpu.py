@@ -108,6 +108,7 @@ def test_attention_clip_at_workload_size():
 @pytest.mark.parametrize("nl,ng", [(16, 0), (0, 16)])
 @pytest.mark.parametrize("F,H,W,C,dt", [
     (600, 3, 4, 128, BF),    # several items per strip, ragged tail
+    (256, 20, 20, 128, BF),  # 800 whole-strip items: several per half, the next one loaded early
     (300, 2, 3, 192, FP),
     (17, 4, 4, 64, BF),      # one window short of a full item
     (5, 3, 3, 64, BF),       # fewer frames than a window

@@ -154,6 +154,8 @@ def test_conv_deterministic():
     (300, 2, 2, 320, BF),    # two query blocks of 256, ragged second block
     (513, 1, 3, 128, BF),    # three blocks, one query in the last
     (70, 3, 1, 128, FP),
+    (256, 20, 20, 320, BF),  # 2000 whole-strip items: several per half, the next one loaded early
+    (400, 16, 16, 128, BF),  # the same with a ragged second block (144 queries)
 ])
 def test_attention_small(F, H, W, C, dt):
     announce(f"attention F={F} H={H} W={W} C={C} dt={dt}")
