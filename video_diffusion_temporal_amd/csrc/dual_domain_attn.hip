@@ -21,7 +21,11 @@
 //     Every HBM load is a full 128-byte row (one cache line) of one frame.
 //   * Scores: q stays in 32 VGPRs as bf16 pairs; 32 keys x 32 v_dot2c each.
 //     The lane holds all 32 scores, so the softmax is lane-local: one max,
-//     exp2 with log2(e)*scale folded in, no cross-lane traffic.
+//     exp2 with log2(e)*scale folded in, no cross-lane traffic.  A K row's
+//     eight 16-byte reads are issued a row ahead and waited for once (one
+//     s_waitcnt per row, not per read: with one computing wave per SIMD
+//     every instruction of that wave costs an issue slot); the weighted sum
+//     does the same per half pair row.
 //   * Weighted sum: 9 local pair rows (the window's parity decides which
 //     pair holds its first frame; the unused slot gets weight 0) and 8 global
 //     pair rows, 64 v_dot2c each, into 64 fp32 accumulators.  The normaliser
@@ -50,7 +54,8 @@
 //   * Pipelining: one persistent 512-thread workgroup per CU owns two LDS
 //     buffers (2 x 80 KB).  Its two 256-thread halves alternate: while one
 //     half stages its next work item (HBM -> LDS, plus its q rows into
-//     registers), the other computes from its own buffer; a workgroup barrier
+//     registers; a whole-strip item issues all its loads before its first
+//     LDS write), the other computes from its own buffer; a workgroup barrier
 //     ends each phase.  HBM traffic and the VALU-bound compute overlap
 //     instead of alternating.
 // Projected kernel (dda_proj_bf16): the Q/K/V projection inside the
@@ -290,7 +295,7 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     constexpr int NLP = NL > 0 ? 9 : 0;         // local V pair rows
     constexpr int NP = NLP + (NG > 0 ? 8 : 0);  // V pair rows
     // Lanes past the last query stay in (the output transpose below moves
-    // data between the 8 lanes of a group) and compute the last query's
+    // data between the 4 lanes of a quad) and compute the last query's
     // windows; their own results are not stored.
     const int tend = g.f0 + g.nq;
     const int t = min(it.t0 + lt, tend - 1);
