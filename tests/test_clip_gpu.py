@@ -32,8 +32,10 @@ def global_rows(F, G=16):
 # ------------------------------------------------------- attention, clips
 
 # F = 600: three work items of 256 query frames per strip, the last ragged;
-# clips shorter than a window, at both ends, and spanning item boundaries.
-CLIPS_600 = [(0, 9), (9, 300), (300, 555), (555, 597), (597, 600), (255, 257), (0, 600)]
+# clips shorter than a window, at both ends, and spanning item boundaries;
+# clip lengths 361 (a ragged second whole-strip item) and 292 (a remainder of
+# 36 queries per strip, four strips to an item).
+CLIPS_600 = [(0, 9), (9, 300), (300, 555), (555, 597), (597, 600), (255, 257), (0, 600), (100, 461), (200, 492)]
 
 
 @pytest.mark.parametrize("dt", [BF, FP])
@@ -108,7 +110,8 @@ def test_attention_clip_at_workload_size():
 @pytest.mark.parametrize("nl,ng", [(16, 0), (0, 16)])
 @pytest.mark.parametrize("F,H,W,C,dt", [
     (600, 3, 4, 128, BF),    # several items per strip, ragged tail
-    (256, 20, 20, 128, BF),  # 800 whole-strip items: several per half, the next one loaded early
+    (256, 20, 20, 128, BF),  # 800 whole-strip items: several per half
+    (292, 2, 3, 64, BF),     # remainder of 36 queries per strip: four strips per item
     (300, 2, 3, 192, FP),
     (17, 4, 4, 64, BF),      # one window short of a full item
     (5, 3, 3, 64, BF),       # fewer frames than a window

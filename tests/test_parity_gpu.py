@@ -154,8 +154,15 @@ def test_conv_deterministic():
     (300, 2, 2, 320, BF),    # two query blocks of 256, ragged second block
     (513, 1, 3, 128, BF),    # three blocks, one query in the last
     (70, 3, 1, 128, FP),
-    (256, 20, 20, 320, BF),  # 2000 whole-strip items: several per half, the next one loaded early
+    (256, 20, 20, 320, BF),  # 2000 whole-strip items: several per half
     (400, 16, 16, 128, BF),  # the same with a ragged second block (144 queries)
+    # remainder packing at its boundaries (F = 256 + r): r = 36 fills four strips' slices, r = 37 takes two,
+    # r = 104 fills two, r = 105 is a partial whole-strip item; F = 255 is one partial item per strip
+    (292, 2, 3, 128, BF),
+    (293, 2, 3, 128, BF),
+    (360, 2, 2, 128, BF),
+    (361, 2, 2, 128, BF),
+    (255, 3, 2, 64, BF),
 ])
 def test_attention_small(F, H, W, C, dt):
     announce(f"attention F={F} H={H} W={W} C={C} dt={dt}")
