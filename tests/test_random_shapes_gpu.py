@@ -81,3 +81,31 @@ def test_random_shape(case):
     q, k, v = x, rnd((F, H, W, C), seed + 2), rnd((F, H, W, C), seed + 3, 0.7)
     o = vinf.dual_domain_attn(upload(q), upload(k), upload(v))
     check(fetch(o), oracle.dda(q, k, v), BF, "attention")
+
+
+FP = synth.F32
+N_FP = 3
+FP_CASES = [draw(100 + i) for i in range(N_FP)]
+
+
+@pytest.mark.parametrize("case", range(N_FP), ids=[f"F{c[0]}_{c[1]}x{c[2]}_C{c[3]}_G{c[4]}" for c in FP_CASES])
+def test_random_shape_f32(case):
+    """The float32 kernels on seeded shapes, every element within 1e-4."""
+    F, H, W, C, G = FP_CASES[case]
+    announce(f"random shape f32 {case}: F={F} {H}x{W} C={C} G={G}")
+    seed = 9500 + 10 * case
+    x = synth.normal(F * H * W * C, seed, FP).reshape(F, H, W, C)
+    w = synth.normal(3 * C * C, seed + 1, FP, (1.0 / (3 * C)) ** 0.5).reshape(3, C, C)
+    y, mean, rstd = vinf.groupnorm_global(upload(x), G)
+    ref, rm, rr = oracle.groupnorm(x, G)
+    check_stats(mean, rstd, rm, rr, "groupnorm stats")
+    check(fetch(y), ref, FP, "groupnorm")
+    xd, wd = upload(x), upload(w)
+    check(fetch(vinf.temporal_conv3(xd, wd)), oracle.conv3(x, w), FP, "conv3")
+    ws = torch.empty(vinf.temporal_conv3_gn_workspace_bytes(C, torch.float32), dtype=torch.uint8, device=xd.device)
+    fused = vinf.temporal_conv3_gn(xd, wd, mean, rstd, workspace=ws)
+    assert np.array_equal(bits(fused), bits(vinf.temporal_conv3(y, wd))), "conv3 with GroupNorm inside"
+    q = x
+    k, v = (synth.normal(F * H * W * C, seed + 2 + i, FP).reshape(F, H, W, C) for i in range(2))
+    o = vinf.dual_domain_attn(upload(q), upload(k), upload(v))
+    check(fetch(o), oracle.dda(q, k, v), FP, "attention")
