@@ -148,7 +148,7 @@ __device__ __forceinline__ void dda_put_pairs(char* dst, const u32x4_t& a, const
 // load before its first LDS write, so its stage costs one memory round trip;
 // the smaller remainder slices write each row kind before loading the next
 // (fewer registers live at once).
-template <int NL, int NG, int R, int NT>
+template <int NL, int NG, int R, int NT, bool QROWS = R == DDA_TQ>
 __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t* __restrict__ q,
                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                           const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
@@ -163,7 +163,24 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
     const int s = it.strip / heads, h = it.strip % heads;
     const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int t = it.t0 + lt;
-    if (t < g.f0 + g.nq) {
+    const int c8 = lt & 7, r0 = lt >> 3;
+    // QROWS (whole-strip items): the q rows of a wave's 64 queries are loaded
+    // as whole 128-byte rows (8 lanes a row, 8 rows an instruction: an eighth
+    // of the cache-line requests of one row per lane) and each lane gets its
+    // own row through LDS, in rows of the K region that only this wave writes
+    // later (its K chunks are rows r0 + RSTEP*i: 8 rows of every 32).  Lanes
+    // past the last query take the last query's row (their results are dropped).
+    static_assert(!QROWS || (ALL_FIRST && NT == 256), "whole q rows: whole-strip items");
+    u32x4_t qw[QROWS ? 8 : 1];
+    auto qtemp = [&](int rq) { return buf + SL::KL + ((lt & ~63) / 8 + RSTEP * (rq >> 3) + (rq & 7)) * DDA_KSTR; };
+    if constexpr (QROWS) {
+        const int tw = it.t0 + (lt & ~63), last = g.f0 + g.nq - 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tr = min(tw + 8 * i + ((lt & 63) >> 3), last);
+            qw[i] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)(tr - g.f0) * rs + col + c8 * 8);
+        }
+    } else if (t < g.f0 + g.nq) {
         const uint16_t* qrow = q + (int64_t)(t - g.f0) * rs + col;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -177,7 +194,6 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
 #pragma unroll
         for (int c = 0; c < 32; ++c) qv[c] = 0u;  // a lane past the last query computes a throw-away copy
     }
-    const int c8 = lt & 7, r0 = lt >> 3;
     // Frames outside [kf0, kend) are not in k/v: their rows are zero-filled
     // (only frames past the video's last frame, or the unused half of a pair
     // row, which carry no weight, fall outside).
@@ -188,6 +204,20 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
 #pragma unroll
         for (int i = 0; i < NIK; ++i)
             if (r0 + RSTEP * i < nkr) *reinterpret_cast<u32x4_t*>(dst + RSTEP * i * DDA_KSTR) = ku[i];
+    };
+    auto q_handover = [&]() {
+        // row 8i + lane/8 of the wave's 64, chunk lane%8, then the lane's own row
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4_t*>(qtemp(8 * i + ((lt & 63) >> 3)) + c8 * 16) = qw[i];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(qtemp(lt & 63) + c * 16);
+            qv[4 * c] = u[0];
+            qv[4 * c + 1] = u[1];
+            qv[4 * c + 2] = u[2];
+            qv[4 * c + 3] = u[3];
+        }
     };
     auto store_v = [&]() {
         char* dst = buf + SL::VP + r0 * DDA_VSTR + c8 * 32;
@@ -241,6 +271,7 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
                 gb[n] = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p + 1) * rs + oc * 8);
             }
         }
+        if constexpr (QROWS) q_handover();
         if constexpr (ALL_FIRST && NL > 0) {
             store_k();
             store_v();
@@ -253,9 +284,12 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
             else if (task < NGTASK)
                 dda_put_pairs(buf + SL::VG + ((task - DDA_G * 8) >> 3) * 256 + (task & 7) * 32, ga[n], gb[n]);
         }
-    } else if constexpr (ALL_FIRST && NL > 0) {
-        store_k();
-        store_v();
+    } else if constexpr (ALL_FIRST) {
+        if constexpr (QROWS) q_handover();
+        if constexpr (NL > 0) {
+            store_k();
+            store_v();
+        }
     }
 }
 
@@ -462,8 +496,13 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
                                              int idx, int lt, uint32_t (&qv)[32]) {
     if (M == 1 || idx < g.nfull) {
         const DdaItem it{idx % g.nstrips, g.f0 + (idx / g.nstrips) * DDA_TQ};
+        // Whole q rows through LDS (QROWS): measured faster for the one-sided
+        // key sets (local only 1.13 -> 1.04-1.07 ms, global only 0.90 -> 0.87-0.89
+        // at F=1024, 64x40x320) but 3% slower for the full key set with
+        // Q = K = V (the extra LDS traffic of the stage competes with the
+        // compute half), and it makes the clip kernels (M > 1) spill.
         if constexpr (STAGE)
-            dda_stage<NL, NG, DDA_TQ, 256>(buf, q, k, v, g, rs, heads, it, lt, qv);
+            dda_stage<NL, NG, DDA_TQ, 256, M == 1 && (NL == 0 || NG == 0)>(buf, q, k, v, g, rs, heads, it, lt, qv);
         else
             dda_compute<NL, NG, DDA_TQ>(buf, o, g, rs, heads, it, lt, qv);
     } else {
