@@ -19,6 +19,9 @@
 //     16 lanes reading neighbouring frames hit distinct banks, and every LDS
 //     read is a per-lane base plus an immediate offset (no address VALU).
 //     Every HBM load is a full 128-byte row (one cache line) of one frame.
+//     A whole-strip item stages without a branch: buffer loads whose range
+//     ends at the last frame in k/v read rows outside it as zero (frames
+//     whose 290 strides fit 32 bits; larger frames guard each load).
 //   * Scores: q stays in 32 VGPRs as bf16 pairs; 32 keys x 32 v_dot2c each.
 //     The lane holds all 32 scores, so the softmax is lane-local: one max,
 //     exp2 with log2(e)*scale folded in, no cross-lane traffic.  A K row's
@@ -293,6 +296,143 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
     }
 }
 
+// Loads at byte offsets outside [0, bytes) of a buffer resource read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dda_rsrc(const uint16_t* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Frame strides for which a whole-strip stage can address its rows with
+// 32-bit buffer offsets (dda_stage_b32): 290 of them below 4 GiB.
+constexpr int64_t DDA_B32_MAX_RS = (int64_t)((1ull << 32) / (290ull * 2ull));
+
+// The stage of a whole-strip item (R = 256 queries, 256 threads) without a
+// branch.  The item's K rows (from its first window frame lo) and V rows
+// (from max(lo & ~1, kf0)) are each one buffer resource whose range ends at
+// kend, so a frame outside [kf0, kend) reads as zero (the row before kf0 has
+// a negative offset, which wraps past the range); every load and store is
+// unconditional.  Rows past the slice (K rows >= KROWS, pairs >= VPAIRS) load
+// and store the slice's last row again: the same value to the same place.
+// Rows past the windows' frames (>= nkr, pairs >= np) are staged but never
+// read.  Lanes past the last query load the last query's row.  Loads are all
+// issued before the first LDS write, as in dda_stage.
+template <int NL, int NG, bool QROWS>
+__device__ __forceinline__ void dda_stage_b32(char* __restrict__ buf, const uint16_t* __restrict__ q,
+                                              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                              const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
+                                              uint32_t (&qv)[32]) {
+    using SL = DdaFull;
+    constexpr int RSTEP = 32;  // rows one pass of the 256 threads covers (8 chunks per row)
+    constexpr int NIK = (SL::KROWS + RSTEP - 1) / RSTEP;
+    constexpr int NIV = (SL::VPAIRS + RSTEP - 1) / RSTEP;
+    static_assert((NIK - 1) * RSTEP + RSTEP - 1 >= SL::KROWS - 1 && (NIK - 1) * RSTEP <= SL::KROWS - 1, "K passes");
+    static_assert((NIV - 1) * RSTEP + RSTEP - 1 >= SL::VPAIRS - 1 && (NIV - 1) * RSTEP <= SL::VPAIRS - 1, "V passes");
+    const int s = it.strip / heads, h = it.strip % heads;
+    const int64_t col = (int64_t)s * g.C + h * DDA_D;
+    const int c8 = lt & 7, r0 = lt >> 3;
+    const int last = g.f0 + g.nq - 1;
+    const uint32_t fb = (uint32_t)rs * 2u;  // frame stride in bytes
+    u32x4_t qw[QROWS ? 8 : 1];
+    if constexpr (QROWS) {
+        // 8 lanes a row, 8 rows an instruction; handed over through LDS below
+        const int tw = it.t0 + (lt & ~63);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tr = min(tw + 8 * i + ((lt & 63) >> 3), last);
+            qw[i] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)(tr - g.f0) * rs + col + c8 * 8);
+        }
+    } else {
+        const uint16_t* qrow = q + (int64_t)(min(it.t0 + lt, last) - g.f0) * rs + col;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(qrow + c * 8);
+            qv[4 * c] = u[0];
+            qv[4 * c + 1] = u[1];
+            qv[4 * c + 2] = u[2];
+            qv[4 * c + 3] = u[3];
+        }
+    }
+    u32x4_t ku[NL > 0 ? NIK : 1], va[NL > 0 ? NIV : 1], vb[NL > 0 ? NIV : 1];
+    if constexpr (NL > 0) {
+        const int lo = dda_start(it.t0, g.F);
+        const int plo = lo & ~1, vf = max(plo, g.kf0);
+        const __amdgpu_buffer_rsrc_t kr =
+            dda_rsrc(k + col + (int64_t)(lo - g.kf0) * rs, (uint32_t)min(g.kend - lo, SL::KROWS) * fb);
+        const __amdgpu_buffer_rsrc_t vr =
+            dda_rsrc(v + col + (int64_t)(vf - g.kf0) * rs, (uint32_t)min(g.kend - vf, 2 * SL::VPAIRS) * fb);
+        const uint32_t ko = (uint32_t)r0 * fb + (uint32_t)c8 * 16u;
+#pragma unroll
+        for (int i = 0; i < NIK; ++i) {
+            const uint32_t off = i < NIK - 1 ? ko + (uint32_t)(RSTEP * i) * fb
+                                             : (uint32_t)min(r0 + RSTEP * i, SL::KROWS - 1) * fb + (uint32_t)c8 * 16u;
+            ku[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)off, 0, 0);
+        }
+        // pair p holds frames plo + 2p and plo + 2p + 1 (plo - vf is 0 or -1)
+        const uint32_t vo = (uint32_t)(plo - vf + 2 * r0) * fb + (uint32_t)c8 * 16u;
+#pragma unroll
+        for (int i = 0; i < NIV; ++i) {
+            const uint32_t off = i < NIV - 1
+                                     ? vo + (uint32_t)(2 * RSTEP * i) * fb
+                                     : (uint32_t)(plo - vf + 2 * min(r0 + RSTEP * i, SL::VPAIRS - 1)) * fb +
+                                           (uint32_t)c8 * 16u;
+            va[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, (int)off, 0, 0);
+            vb[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, (int)(off + fb), 0, 0);
+        }
+    }
+    constexpr int NGTASK = DDA_G * 8 + (DDA_G / 2) * 8;  // global K row chunks, then V pair chunks
+    static_assert(NGTASK <= 256, "one global task per thread");
+    u32x4_t ga = u32x4_t{0u, 0u, 0u, 0u}, gb = ga;
+    if constexpr (NG > 0) {
+        const uint16_t* kgb = g.kg ? static_cast<const uint16_t*>(g.kg) : k;
+        const uint16_t* vgb = g.vg ? static_cast<const uint16_t*>(g.vg) : v;
+        auto grow = [&](int i) -> int64_t {  // row of global frame i in kgb / vgb
+            return g.kg ? (int64_t)i : (int64_t)(((int64_t)i * g.F) / DDA_G) - g.kf0;
+        };
+        // wave-uniform: waves 0-1 the K rows, wave 2 the V pairs, wave 3 none
+        if (lt < DDA_G * 8) {
+            ga = *reinterpret_cast<const u32x4_t*>(kgb + col + grow(lt >> 3) * rs + c8 * 8);
+        } else if (lt < NGTASK) {
+            const int p = (lt - DDA_G * 8) >> 3;
+            ga = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p) * rs + c8 * 8);
+            gb = *reinterpret_cast<const u32x4_t*>(vgb + col + grow(2 * p + 1) * rs + c8 * 8);
+        }
+    }
+    if constexpr (QROWS) {
+        // row 8i + lane/8 of the wave's 64, chunk lane%8, then the lane's own
+        // row, in K rows that only this wave writes later (its K chunks are
+        // rows r0 + 32i: 8 rows of every 32)
+        auto qtemp = [&](int rq) { return buf + SL::KL + ((lt & ~63) / 8 + RSTEP * (rq >> 3) + (rq & 7)) * DDA_KSTR; };
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4_t*>(qtemp(8 * i + ((lt & 63) >> 3)) + c8 * 16) = qw[i];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(qtemp(lt & 63) + c * 16);
+            qv[4 * c] = u[0];
+            qv[4 * c + 1] = u[1];
+            qv[4 * c + 2] = u[2];
+            qv[4 * c + 3] = u[3];
+        }
+    }
+    if constexpr (NL > 0) {
+        char* kd = buf + SL::KL + r0 * DDA_KSTR + c8 * 16;
+#pragma unroll
+        for (int i = 0; i < NIK - 1; ++i) *reinterpret_cast<u32x4_t*>(kd + RSTEP * i * DDA_KSTR) = ku[i];
+        *reinterpret_cast<u32x4_t*>(buf + SL::KL + min(r0 + RSTEP * (NIK - 1), SL::KROWS - 1) * DDA_KSTR + c8 * 16) =
+            ku[NIK - 1];
+        char* vd = buf + SL::VP + r0 * DDA_VSTR + c8 * 32;
+#pragma unroll
+        for (int i = 0; i < NIV - 1; ++i) dda_put_pairs(vd + RSTEP * i * DDA_VSTR, va[i], vb[i]);
+        dda_put_pairs(buf + SL::VP + min(r0 + RSTEP * (NIV - 1), SL::VPAIRS - 1) * DDA_VSTR + c8 * 32, va[NIV - 1],
+                      vb[NIV - 1]);
+    }
+    if constexpr (NG > 0) {
+        if (lt < DDA_G * 8)
+            *reinterpret_cast<u32x4_t*>(buf + SL::KG + (lt >> 3) * 128 + c8 * 16) = ga;
+        else if (lt < NGTASK)
+            dda_put_pairs(buf + SL::VG + ((lt - DDA_G * 8) >> 3) * 256 + c8 * 32, ga, gb);
+    }
+}
+
 // a.x*b.x + a.y*b.y for bf16 pairs, fp32 (the three-operand v_dot2_f32_bf16
 // with a zero addend: a chain starts without a zeroed accumulator).
 __device__ __forceinline__ float dot2_zero(uint32_t a, uint32_t b) {
@@ -489,7 +629,7 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 // the rest are remainder items of M strips (s0 .. s0+M-1) x the last
 // nq - 256*nchunks queries, strip j in slice j of the buffer, threads
 // 256/M*j .. 256/M*(j+1)-1 (waves 4/M*j ..) on it.
-template <int NL, int NG, int M, bool STAGE>
+template <int NL, int NG, int M, bool B32, bool STAGE>
 __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint16_t* __restrict__ q,
                                              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                              uint16_t* __restrict__ o, const DdaGeo& g, int64_t rs, int heads,
@@ -501,8 +641,11 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
         // at F=1024, 64x40x320) but 3% slower for the full key set with
         // Q = K = V (the extra LDS traffic of the stage competes with the
         // compute half), and it makes the clip kernels (M > 1) spill.
-        if constexpr (STAGE)
-            dda_stage<NL, NG, DDA_TQ, 256, M == 1 && (NL == 0 || NG == 0)>(buf, q, k, v, g, rs, heads, it, lt, qv);
+        constexpr bool QROWS = M == 1 && (NL == 0 || NG == 0);
+        if constexpr (STAGE && B32)
+            dda_stage_b32<NL, NG, QROWS>(buf, q, k, v, g, rs, heads, it, lt, qv);
+        else if constexpr (STAGE)
+            dda_stage<NL, NG, DDA_TQ, 256, QROWS>(buf, q, k, v, g, rs, heads, it, lt, qv);
         else
             dda_compute<NL, NG, DDA_TQ>(buf, o, g, rs, heads, it, lt, qv);
     } else {
@@ -524,7 +667,7 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
 // Phase p: half 0 stages its item p/2 (p even) or computes item (p-1)/2 (p
 // odd); half 1 stages item (p-1)/2 (p odd) or computes item (p-2)/2 (p even,
 // p >= 2).  Every thread runs every phase and barrier.
-template <int NL, int NG, int M>
+template <int NL, int NG, int M, bool B32>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
          uint16_t* __restrict__ o, DdaGeo g) {
@@ -546,9 +689,9 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
             if (j < jh) {
                 const int idx = w + (2 * j + half) * G;
                 if ((rel & 1) == 0)
-                    dda_item_run<NL, NG, M, true>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
+                    dda_item_run<NL, NG, M, B32, true>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
                 else
-                    dda_item_run<NL, NG, M, false>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
+                    dda_item_run<NL, NG, M, B32, false>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
             }
         }
         __syncthreads();
@@ -929,14 +1072,23 @@ vinf_status launch_dda(const void* q, const void* k, const void* v, const void* 
         const uint16_t *qb = static_cast<const uint16_t*>(q), *kb = static_cast<const uint16_t*>(k),
                        *vb = static_cast<const uint16_t*>(v);
         uint16_t* ob = static_cast<uint16_t*>(o);
-        auto run = [&](auto nl, auto ng) {
+        // whole-strip stages with 32-bit buffer offsets unless a frame is too large
+        const bool b32 = (int64_t)S * C <= DDA_B32_MAX_RS;
+        auto run2 = [&](auto nl, auto ng, auto b) {
             constexpr int NL = decltype(nl)::value, NG = decltype(ng)::value;
+            constexpr bool B = decltype(b)::value;
             if (M == 4)
-                hipLaunchKernelGGL((dda_bf16<NL, NG, 4>), grid, block, 0, st, qb, kb, vb, ob, g);
+                hipLaunchKernelGGL((dda_bf16<NL, NG, 4, B>), grid, block, 0, st, qb, kb, vb, ob, g);
             else if (M == 2)
-                hipLaunchKernelGGL((dda_bf16<NL, NG, 2>), grid, block, 0, st, qb, kb, vb, ob, g);
+                hipLaunchKernelGGL((dda_bf16<NL, NG, 2, B>), grid, block, 0, st, qb, kb, vb, ob, g);
             else
-                hipLaunchKernelGGL((dda_bf16<NL, NG, 1>), grid, block, 0, st, qb, kb, vb, ob, g);
+                hipLaunchKernelGGL((dda_bf16<NL, NG, 1, B>), grid, block, 0, st, qb, kb, vb, ob, g);
+        };
+        auto run = [&](auto nl, auto ng) {
+            if (b32)
+                run2(nl, ng, std::true_type{});
+            else
+                run2(nl, ng, std::false_type{});
         };
         using K16 = std::integral_constant<int, DDA_L>;
         using K0 = std::integral_constant<int, 0>;
