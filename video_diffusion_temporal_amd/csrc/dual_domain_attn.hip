@@ -150,7 +150,8 @@ __device__ __forceinline__ void dda_put_pairs(char* dst, const u32x4_t& a, const
 // rows, and global-row tasks lt + NT*n.  A full item (R = 256) issues every
 // load before its first LDS write, so its stage costs one memory round trip;
 // the smaller remainder slices write each row kind before loading the next
-// (fewer registers live at once).
+// (fewer registers live at once).  Whole-strip items use this stage only for
+// frames too large for dda_stage_b32's 32-bit offsets.
 template <int NL, int NG, int R, int NT, bool QROWS = R == DDA_TQ>
 __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t* __restrict__ q,
                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
