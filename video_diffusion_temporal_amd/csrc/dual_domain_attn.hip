@@ -60,7 +60,8 @@
 //     registers; a whole-strip item issues all its loads before its first
 //     LDS write), the other computes from its own buffer; a workgroup barrier
 //     ends each phase.  HBM traffic and the VALU-bound compute overlap
-//     instead of alternating.
+//     instead of alternating.  The computing waves run at raised wave
+//     priority (s_setprio), so they issue first on their SIMDs.
 // Projected kernel (dda_proj_bf16): the Q/K/V projection inside the
 // attention's work items (see its comment below).
 // fp32 kernel (dda_f32): one query per thread, fp32 FMA, keys read through
@@ -625,6 +626,22 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     }
 }
 
+// The compute of an item at raised wave priority.  Each SIMD holds one wave
+// of each half; when both have an instruction ready, the computing wave (the
+// phase's critical path) issues first and the staging wave fills its gaps.
+// Measured at F=1024, 64x40x320, one box, three alternating pairs of whole
+// runs: chain attention 1.57-1.62 against 1.60-1.65 ms, distinct Q/K/V within
+// 1%.  (A wave's priority is a hint to the CU's instruction arbiter; the
+// stream's priority is untouched.)
+template <int NL, int NG, int R>
+__device__ __forceinline__ void dda_compute_prio(const char* __restrict__ buf, uint16_t* __restrict__ o,
+                                                 const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
+                                                 uint32_t (&qv)[32]) {
+    __builtin_amdgcn_s_setprio(1);
+    dda_compute<NL, NG, R>(buf, o, g, rs, heads, it, lt, qv);
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // One work item of a half workgroup (256 threads, lt = 0..255): stage it
 // (STAGE) or compute it.  Items below g.nfull are one strip x 256 queries;
 // the rest are remainder items of M strips (s0 .. s0+M-1) x the last
@@ -648,7 +665,7 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
         else if constexpr (STAGE)
             dda_stage<NL, NG, DDA_TQ, 256, QROWS>(buf, q, k, v, g, rs, heads, it, lt, qv);
         else
-            dda_compute<NL, NG, DDA_TQ>(buf, o, g, rs, heads, it, lt, qv);
+            dda_compute_prio<NL, NG, DDA_TQ>(buf, o, g, rs, heads, it, lt, qv);
     } else {
         constexpr int R = DdaRemR<M>, NT = 256 / M;
         const int j = lt / NT, ls = lt % NT;
@@ -658,7 +675,7 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
         if constexpr (STAGE)
             dda_stage<NL, NG, R, NT>(slice, q, k, v, g, rs, heads, it, ls, qv);
         else
-            dda_compute<NL, NG, R>(slice, o, g, rs, heads, it, ls, qv);
+            dda_compute_prio<NL, NG, R>(slice, o, g, rs, heads, it, ls, qv);
     }
 }
 
