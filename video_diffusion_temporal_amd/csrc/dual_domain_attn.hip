@@ -513,6 +513,15 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
         sc[i] = a;
     }
 
+    // The weighted sum's first half pair row is read now, so that the
+    // softmax below covers its latency (the scheduling barrier keeps the
+    // reads here).
+    const char* vrow0 = NLP > 0 ? buf + SL::VP + ((st - plo) >> 1) * DDA_VSTR : buf + SL::VG;
+    u32x4_t vfirst[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vfirst[c] = *reinterpret_cast<const u32x4_t*>(vrow0 + c * 16);
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---- lane-local softmax (base 2, scale folded in) ----
     // (the maximum is taken before the scaling: sl2e > 0 keeps the order)
     float m = -INFINITY;
@@ -558,7 +567,7 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // dims 32*hh.. of pair row j; one wait per step
     u32x4_t vb[2][8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) vb[0][c] = *reinterpret_cast<const u32x4_t*>(val_row(0) + c * 16);
+    for (int c = 0; c < 8; ++c) vb[0][c] = vfirst[c];  // val_row(0), read before the softmax
 #pragma unroll
     for (int step = 0; step < 2 * NP; ++step) {
         const int j = step >> 1, hh = step & 1;
@@ -584,7 +593,8 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // each half of their 8 x 16-byte chunks (xor-butterfly over lane
     // distances 2, 1), so that a store writes 64 contiguous bytes (half a
     // head row) of each of 16 frames instead of 16 bytes of each of 64 ----
-    const float inv = 1.f / den;
+    // hardware reciprocal (1 ulp); den >= 1, as the largest weight is exactly 1
+    const float inv = __builtin_amdgcn_rcpf(den);
     uint32_t ov[8][4];  // ov[c]: channels 8c .. 8c+7, bf16 pairs
 #pragma unroll
     for (int c = 0; c < 8; ++c)
