@@ -604,22 +604,27 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // One butterfly stage over lane distance j within each quad: the lower
     // lane takes the partner's chunk c0 into slot c0+j, the upper lane the
     // partner's chunk c0+j into slot c0 (ds_swizzle reads the partner).
+    // The 16 exchanges of a stage are issued back to back (all sends first,
+    // a scheduling barrier, all swizzles), so their latencies overlap.
     auto stage = [&](auto dist) {
         constexpr int j = decltype(dist)::value;
         constexpr int pattern = 0x1f | (j << 10);  // ds_swizzle bit mode: lane ^ j
         const bool upper = (lb & j) != 0;
+        uint32_t x[16];
 #pragma unroll
-        for (int c0 = 0; c0 < 8; ++c0) {
-            if (c0 & j) continue;
+        for (int n = 0; n < 16; ++n) {
+            const int c0 = ((n >> 2) / j) * 2 * j + (n >> 2) % j, e = n & 3;  // the 4 slots c0 with c0 & j == 0
+            x[n] = upper ? ov[c0][e] : ov[c0 + j][e];
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t send = upper ? ov[c0][e] : ov[c0 + j][e];
-                const uint32_t got = (uint32_t)__builtin_amdgcn_ds_swizzle((int)send, pattern);
-                if (upper)
-                    ov[c0][e] = got;
-                else
-                    ov[c0 + j][e] = got;
-            }
+        for (int n = 0; n < 16; ++n) x[n] = (uint32_t)__builtin_amdgcn_ds_swizzle((int)x[n], pattern);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const int c0 = ((n >> 2) / j) * 2 * j + (n >> 2) % j, e = n & 3;
+            ov[c0][e] = upper ? x[n] : ov[c0][e];          // value selects: every index stays static
+            ov[c0 + j][e] = upper ? ov[c0 + j][e] : x[n];
         }
     };
     stage(std::integral_constant<int, 2>{});
