@@ -133,7 +133,12 @@ struct DdaGeo {
 
 struct DdaItem {
     int strip, t0;
+    int s, h;  // location and head of the strip (strip = s * heads + h)
 };
+
+__device__ __forceinline__ DdaItem dda_item(int strip, int t0, int heads) {
+    return DdaItem{strip, t0, strip / heads, strip % heads};
+}
 
 // V rows f, f+1 (16 bytes each, 8 dims) -> two 16-byte pair chunks
 // (v[f][d], v[f+1][d]) in LDS at dst.
@@ -165,7 +170,7 @@ __device__ __forceinline__ void dda_stage(char* __restrict__ buf, const uint16_t
     constexpr int NIV = NL > 0 ? (SL::VPAIRS + RSTEP - 1) / RSTEP : 1;
     constexpr int NGTASK = DDA_G * 8 + (DDA_G / 2) * 8;  // global K row chunks, then V pair chunks
     constexpr int NGT = NG > 0 ? (NGTASK + NT - 1) / NT : 1;
-    const int s = it.strip / heads, h = it.strip % heads;
+    const int s = it.s, h = it.h;
     const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int t = it.t0 + lt;
     const int c8 = lt & 7, r0 = lt >> 3;
@@ -328,7 +333,7 @@ __device__ __forceinline__ void dda_stage_b32(char* __restrict__ buf, const uint
     constexpr int NIV = (SL::VPAIRS + RSTEP - 1) / RSTEP;
     static_assert((NIK - 1) * RSTEP + RSTEP - 1 >= SL::KROWS - 1 && (NIK - 1) * RSTEP <= SL::KROWS - 1, "K passes");
     static_assert((NIV - 1) * RSTEP + RSTEP - 1 >= SL::VPAIRS - 1 && (NIV - 1) * RSTEP <= SL::VPAIRS - 1, "V passes");
-    const int s = it.strip / heads, h = it.strip % heads;
+    const int s = it.s, h = it.h;
     const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int c8 = lt & 7, r0 = lt >> 3;
     const int last = g.f0 + g.nq - 1;
@@ -475,7 +480,7 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // windows; their own results are not stored.
     const int tend = g.f0 + g.nq;
     const int t = min(it.t0 + lt, tend - 1);
-    const int s = it.strip / heads, h = it.strip % heads;
+    const int s = it.s, h = it.h;
     const int64_t col = (int64_t)s * g.C + h * DDA_D;
     const int F = g.F;
     const int lo = dda_start(it.t0, F);
@@ -666,9 +671,12 @@ template <int NL, int NG, int M, bool B32, bool STAGE>
 __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint16_t* __restrict__ q,
                                              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                              uint16_t* __restrict__ o, const DdaGeo& g, int64_t rs, int heads,
-                                             int idx, int lt, uint32_t (&qv)[32]) {
+                                             int idx, int lt, uint32_t (&qv)[32], DdaItem& cur) {
+    // The stage works out the item's coordinates (integer divisions) and
+    // the compute of the same item, a phase later, reuses them.
     if (M == 1 || idx < g.nfull) {
-        const DdaItem it{idx % g.nstrips, g.f0 + (idx / g.nstrips) * DDA_TQ};
+        if constexpr (STAGE) cur = dda_item(idx % g.nstrips, g.f0 + (idx / g.nstrips) * DDA_TQ, heads);
+        const DdaItem it = cur;
         // Whole q rows through LDS (QROWS): measured faster for the one-sided
         // key sets (local only 1.13 -> 1.04-1.07 ms, global only 0.90 -> 0.87-0.89
         // at F=1024, 64x40x320) but 3% slower for the full key set with
@@ -684,7 +692,8 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
     } else {
         constexpr int R = DdaRemR<M>, NT = 256 / M;
         const int j = lt / NT, ls = lt % NT;
-        const DdaItem it{(idx - g.nfull) * M + j, g.f0 + g.nchunks * DDA_TQ};
+        if constexpr (STAGE) cur = dda_item((idx - g.nfull) * M + j, g.f0 + g.nchunks * DDA_TQ, heads);
+        const DdaItem it = cur;
         if (it.strip >= g.nstrips) return;  // the last remainder item may hold fewer strips
         char* slice = buf + j * DdaSlice<R>::BYTES;
         if constexpr (STAGE)
@@ -715,6 +724,7 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     const int j0 = (mine + 1) / 2, j1 = mine / 2;
     const int phases = max(2 * j0, 2 * j1 + 1);
     uint32_t qv[32];
+    DdaItem cur{0, 0, 0, 0};  // the half's current item, from its stage to its compute
     for (int p = 0; p < phases; ++p) {
         const int rel = p - half;                 // half 0: rel = p, half 1: rel = p - 1
         if (rel >= 0) {
@@ -722,9 +732,9 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
             if (j < jh) {
                 const int idx = w + (2 * j + half) * G;
                 if ((rel & 1) == 0)
-                    dda_item_run<NL, NG, M, B32, true>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
+                    dda_item_run<NL, NG, M, B32, true>(buf, q, k, v, o, g, rs, heads, idx, lt, qv, cur);
                 else
-                    dda_item_run<NL, NG, M, B32, false>(buf, q, k, v, o, g, rs, heads, idx, lt, qv);
+                    dda_item_run<NL, NG, M, B32, false>(buf, q, k, v, o, g, rs, heads, idx, lt, qv, cur);
             }
         }
         __syncthreads();
@@ -798,8 +808,8 @@ dda_proj_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, co
     for (int k = 0;; ++k) {
         const int idx = item_of(k);
         if (idx < 0) break;
-        const DdaItem it{idx % g.nstrips, (idx / g.nstrips) * DDA_TQ};
-        const int s = it.strip / heads, h = it.strip % heads;
+        const DdaItem it = dda_item(idx % g.nstrips, (idx / g.nstrips) * DDA_TQ, heads);
+        const int s = it.s, h = it.h;
         const int F = g.F;
         const int lo = dda_start(it.t0, F);
         const int tlast = min(it.t0 + DDA_TQ, F) - 1;
