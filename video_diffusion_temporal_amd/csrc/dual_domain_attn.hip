@@ -467,7 +467,8 @@ __device__ __forceinline__ void lds_wait(int n) {
 }
 
 // Compute query t0 + lt of a strip staged in slice `buf` (layout DdaSlice<R>).
-template <int NL, int NG, int R>
+// SHORT: the video may have fewer frames than the local window.
+template <int NL, int NG, int R, bool SHORT = true>
 __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16_t* __restrict__ o,
                                             const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
                                             const uint32_t (&qv)[32]) {
@@ -497,6 +498,7 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
         return i < NL ? krow + i * DDA_KSTR : buf + SL::KG + (i - NL) * 128;
     };
     u32x4_t kb[2][8];
+    uint32_t klast = 0;  // last dword of the previous K row
 #pragma unroll
     for (int c = 0; c < 8; ++c) kb[0][c] = *reinterpret_cast<const u32x4_t*>(key_row(0) + c * 16);
 #pragma unroll
@@ -507,16 +509,22 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
         }
         lds_wait(i + 1 < NK ? 8 : 0);  // row i has landed; row i+1's 8 reads may be in flight
         float a = dot2_zero(qv[0], kb[i & 1][0][0]);
+        // the previous row's last product goes between this zero-addend
+        // dot2 and the first use of its result (which would otherwise wait
+        // one cycle); each score still sums its products in order
+        if (i > 0) sc[i - 1] = dot2_bf16(qv[31], klast, sc[i - 1]);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const u32x4_t u = kb[i & 1][c];
             if (c > 0) a = dot2_bf16(qv[4 * c], u[0], a);
             a = dot2_bf16(qv[4 * c + 1], u[1], a);
             a = dot2_bf16(qv[4 * c + 2], u[2], a);
-            a = dot2_bf16(qv[4 * c + 3], u[3], a);
+            if (c < 7) a = dot2_bf16(qv[4 * c + 3], u[3], a);
         }
+        klast = kb[i & 1][7][3];
         sc[i] = a;
     }
+    sc[NK - 1] = dot2_bf16(qv[31], klast, sc[NK - 1]);
 
     // The weighted sum's first half pair row is read now, so that the
     // softmax below covers its latency (the scheduling barrier keeps the
@@ -529,10 +537,12 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 
     // ---- lane-local softmax (base 2, scale folded in) ----
     // (the maximum is taken before the scaling: sl2e > 0 keeps the order)
+    // A video shorter than the window has nl < 16 local keys: the rest are
+    // masked out (SHORT; a whole-strip item has 256 query frames, so 16).
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-        sc[j] = (j < NL && j >= nl) ? -INFINITY : sc[j];
+        if (SHORT) sc[j] = (j < NL && j >= nl) ? -INFINITY : sc[j];
         m = fmaxf(m, sc[j]);
     }
     const float msl = -(m * g.sl2e);
@@ -624,7 +634,7 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < 16; ++n) x[n] = (uint32_t)__builtin_amdgcn_ds_swizzle((int)x[n], pattern);
-        __builtin_amdgcn_sched_barrier(0);
+        lds_wait(0);  // one wait for the 16 exchanges, not one per use
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             const int c0 = ((n >> 2) / j) * 2 * j + (n >> 2) % j, e = n & 3;
@@ -637,12 +647,24 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // lane 4a+b now holds chunks b and b+4 of frames 4a .. 4a+3 (slot k:
     // frame 4a + k%4, chunk b + 4*(k/4))
     const int tg = it.t0 + (lt & ~3);
+    if (tg + 3 < tend) {
+        // every frame of the quad is a query (all but the video's last
+        // quad): 8 stores from one address, no branch per store
+        uint16_t* ob = o + (int64_t)(tg - g.f0) * rs + col + lb * 8;
 #pragma unroll
-    for (int kf = 0; kf < 8; ++kf) {
-        const int tf = tg + (kf & 3);
-        if (tf < tend)
-            *reinterpret_cast<u32x4_t*>(o + (int64_t)(tf - g.f0) * rs + col + (lb + 4 * (kf >> 2)) * 8) =
-                u32x4_t{ov[kf][0], ov[kf][1], ov[kf][2], ov[kf][3]};
+        for (int kq = 0; kq < 4; ++kq) {
+            uint16_t* p = ob + (int64_t)kq * rs;
+            *reinterpret_cast<u32x4_t*>(p) = u32x4_t{ov[kq][0], ov[kq][1], ov[kq][2], ov[kq][3]};
+            *reinterpret_cast<u32x4_t*>(p + 32) = u32x4_t{ov[kq + 4][0], ov[kq + 4][1], ov[kq + 4][2], ov[kq + 4][3]};
+        }
+    } else {
+#pragma unroll
+        for (int kf = 0; kf < 8; ++kf) {
+            const int tf = tg + (kf & 3);
+            if (tf < tend)
+                *reinterpret_cast<u32x4_t*>(o + (int64_t)(tf - g.f0) * rs + col + (lb + 4 * (kf >> 2)) * 8) =
+                    u32x4_t{ov[kf][0], ov[kf][1], ov[kf][2], ov[kf][3]};
+        }
     }
 }
 
@@ -653,12 +675,12 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
 // runs: chain attention 1.57-1.62 against 1.60-1.65 ms, distinct Q/K/V within
 // 1%.  (A wave's priority is a hint to the CU's instruction arbiter; the
 // stream's priority is untouched.)
-template <int NL, int NG, int R>
+template <int NL, int NG, int R, bool SHORT>
 __device__ __forceinline__ void dda_compute_prio(const char* __restrict__ buf, uint16_t* __restrict__ o,
                                                  const DdaGeo& g, int64_t rs, int heads, DdaItem it, int lt,
                                                  uint32_t (&qv)[32]) {
     __builtin_amdgcn_s_setprio(1);
-    dda_compute<NL, NG, R>(buf, o, g, rs, heads, it, lt, qv);
+    dda_compute<NL, NG, R, SHORT>(buf, o, g, rs, heads, it, lt, qv);
     __builtin_amdgcn_s_setprio(0);
 }
 
@@ -688,7 +710,7 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
         else if constexpr (STAGE)
             dda_stage<NL, NG, DDA_TQ, 256, QROWS>(buf, q, k, v, g, rs, heads, it, lt, qv);
         else
-            dda_compute_prio<NL, NG, DDA_TQ>(buf, o, g, rs, heads, it, lt, qv);
+            dda_compute_prio<NL, NG, DDA_TQ, false>(buf, o, g, rs, heads, it, lt, qv);
     } else {
         constexpr int R = DdaRemR<M>, NT = 256 / M;
         const int j = lt / NT, ls = lt % NT;
@@ -699,7 +721,7 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
         if constexpr (STAGE)
             dda_stage<NL, NG, R, NT>(slice, q, k, v, g, rs, heads, it, ls, qv);
         else
-            dda_compute_prio<NL, NG, R>(slice, o, g, rs, heads, it, ls, qv);
+            dda_compute_prio<NL, NG, R, true>(slice, o, g, rs, heads, it, ls, qv);
     }
 }
 
