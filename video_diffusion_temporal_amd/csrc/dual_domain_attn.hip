@@ -54,6 +54,10 @@
 //     (a clip of 288 frames: 32), M strips share one item (M = 4 for r <= 36,
 //     2 for r <= 104), each in its own slice of the buffer with 4/M waves, so
 //     a short remainder does not cost a whole item per strip.
+//   * Item order: items are numbered strip-major (a strip's frame chunks in
+//     a row) and every workgroup takes a contiguous range, so consecutive
+//     items of a workgroup are neighbouring chunks of one strip whose shared
+//     window frames come from L2.
 //   * Pipelining: one persistent 512-thread workgroup per CU owns two LDS
 //     buffers (2 x 80 KB).  Its two 256-thread halves alternate: while one
 //     half stages its next work item (HBM -> LDS, plus its q rows into
@@ -697,7 +701,8 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
     // The stage works out the item's coordinates (integer divisions) and
     // the compute of the same item, a phase later, reuses them.
     if (M == 1 || idx < g.nfull) {
-        if constexpr (STAGE) cur = dda_item(idx % g.nstrips, g.f0 + (idx / g.nstrips) * DDA_TQ, heads);
+        // strip-major: consecutive items are consecutive frame chunks of one strip
+        if constexpr (STAGE) cur = dda_item(idx / g.nchunks, g.f0 + (idx % g.nchunks) * DDA_TQ, heads);
         const DdaItem it = cur;
         // Whole q rows through LDS (QROWS): measured faster for the one-sided
         // key sets (local only 1.13 -> 1.04-1.07 ms, global only 0.90 -> 0.87-0.89
@@ -725,9 +730,10 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
     }
 }
 
-// Persistent, two-phase pipelined kernel: workgroup w takes items
-// w, w + G, w + 2G, ... (G = gridDim.x); its half g (threads 256g..256g+255)
-// takes the items with odd (g = 1) or even (g = 0) position in that list.
+// Persistent, two-phase pipelined kernel: workgroup w takes a contiguous
+// range of the item list (G = gridDim.x workgroups share it evenly); its half
+// g (threads 256g..256g+255) takes the items with odd (g = 1) or even (g = 0)
+// position in that range.
 // Phase p: half 0 stages its item p/2 (p even) or computes item (p-1)/2 (p
 // odd); half 1 stages item (p-1)/2 (p odd) or computes item (p-2)/2 (p even,
 // p >= 2).  Every thread runs every phase and barrier.
@@ -741,7 +747,11 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), lt = threadIdx.x & 255;
     char* buf = lds + half * DDA_LDS_BYTES;
     const int G = gridDim.x, w = blockIdx.x;
-    const int mine = w < g.nitems ? (g.nitems - w + G - 1) / G : 0;  // items of this workgroup
+    // Items b0 .. b0+mine-1 of the list: a contiguous range, so the two
+    // halves stage neighbouring frame chunks of a strip in neighbouring
+    // phases and the 15 frames their windows share come from L2.
+    const int b0 = (int)(((int64_t)g.nitems * w) / G);
+    const int mine = (int)(((int64_t)g.nitems * (w + 1)) / G) - b0;  // items of this workgroup
     const int jh = (mine - half + 1) / 2;                             // items of this half
     const int j0 = (mine + 1) / 2, j1 = mine / 2;
     const int phases = max(2 * j0, 2 * j1 + 1);
@@ -752,7 +762,7 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         if (rel >= 0) {
             const int j = rel >> 1;
             if (j < jh) {
-                const int idx = w + (2 * j + half) * G;
+                const int idx = b0 + 2 * j + half;
                 if ((rel & 1) == 0)
                     dda_item_run<NL, NG, M, B32, true>(buf, q, k, v, o, g, rs, heads, idx, lt, qv, cur);
                 else
