@@ -126,7 +126,9 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __b
 // is frame floor(i*F/16)) or are null when k and v hold those frames.  The
 // whole video on its own is f0 = kf0 = 0, nq = kend = F, kg = vg = null.
 // Work items: nfull = nstrips * nchunks items of (strip, 256 query frames
-// from f0 + 256*chunk), then the remainder items (packed kernels only).
+// from f0 + 256*chunk), numbered strip * nchunks + chunk in dda_bf16 and
+// chunk * nstrips + strip in the projected kernel, then the remainder items
+// (packed kernels only).
 struct DdaGeo {
     const void* kg;
     const void* vg;
