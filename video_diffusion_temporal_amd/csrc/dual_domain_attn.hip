@@ -134,6 +134,7 @@ struct DdaGeo {
     const void* vg;
     int F, f0, nq, kf0, kend;
     int S, C, nstrips, nchunks, nfull, nitems;
+    int chunk_major;  // dda_bf16 item order (below)
     float sl2e;
 };
 
@@ -703,8 +704,13 @@ __device__ __forceinline__ void dda_item_run(char* __restrict__ buf, const uint1
     // The stage works out the item's coordinates (integer divisions) and
     // the compute of the same item, a phase later, reuses them.
     if (M == 1 || idx < g.nfull) {
-        // strip-major: consecutive items are consecutive frame chunks of one strip
-        if constexpr (STAGE) cur = dda_item(idx / g.nchunks, g.f0 + (idx % g.nchunks) * DDA_TQ, heads);
+        if constexpr (STAGE) {
+            // item idx of the strip-major list (a strip's frame chunks in a
+            // row) or of the chunk-major one
+            const int strip = g.chunk_major ? idx % g.nstrips : idx / g.nchunks;
+            const int chunk = g.chunk_major ? idx / g.nstrips : idx % g.nchunks;
+            cur = dda_item(strip, g.f0 + chunk * DDA_TQ, heads);
+        }
         const DdaItem it = cur;
         // Whole q rows through LDS (QROWS): measured faster for the one-sided
         // key sets (local only 1.13 -> 1.04-1.07 ms, global only 0.90 -> 0.87-0.89
@@ -749,11 +755,17 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), lt = threadIdx.x & 255;
     char* buf = lds + half * DDA_LDS_BYTES;
     const int G = gridDim.x, w = blockIdx.x;
-    // Items b0 .. b0+mine-1 of the list: a contiguous range, so the two
-    // halves stage neighbouring frame chunks of a strip in neighbouring
-    // phases and the 15 frames their windows share come from L2.
-    const int b0 = (int)(((int64_t)g.nitems * w) / G);
-    const int mine = (int)(((int64_t)g.nitems * (w + 1)) / G) - b0;  // items of this workgroup
+    // Items b0 .. b0+mine-1 of the strip-major list: a contiguous range, so
+    // the two halves stage neighbouring frame chunks of a strip in
+    // neighbouring phases and the 15 frames their windows share come from L2.
+    // With Q = K = V and the full key set (chunk_major) every row is read
+    // three times within its own stage anyway, and items w, w + G, w + 2G,
+    // ... of the chunk-major list measured faster: the workgroups then stage
+    // neighbouring strips.  (The one-sided key sets are slower that way.)
+    const int b0 = g.chunk_major ? w : (int)(((int64_t)g.nitems * w) / G);
+    const int mine = g.chunk_major ? (w < g.nitems ? (g.nitems - w + G - 1) / G : 0)
+                                   : (int)(((int64_t)g.nitems * (w + 1)) / G) - b0;  // items of this workgroup
+    const int stride = g.chunk_major ? G : 1;
     const int jh = (mine - half + 1) / 2;                             // items of this half
     const int j0 = (mine + 1) / 2, j1 = mine / 2;
     const int phases = max(2 * j0, 2 * j1 + 1);
@@ -764,7 +776,7 @@ dda_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         if (rel >= 0) {
             const int j = rel >> 1;
             if (j < jh) {
-                const int idx = b0 + 2 * j + half;
+                const int idx = b0 + (2 * j + half) * stride;
                 if ((rel & 1) == 0)
                     dda_item_run<NL, NG, M, B32, true>(buf, q, k, v, o, g, rs, heads, idx, lt, qv, cur);
                 else
@@ -1096,6 +1108,7 @@ vinf_status launch_dda_projected(const void* x, const void* w, const float* bias
     g.nstrips = (int)nstrips;
     g.nchunks = (int)nchunks;
     g.nfull = g.nitems = (int)(nstrips * nchunks);
+    g.chunk_major = 0;
     if ((uint64_t)F * S * C * 2 > 0xffffffffull)
         return fail(VINF_ERR_UNSUPPORTED, "projected_dual_domain_attn: x of 4 GiB or more (32-bit buffer offsets)");
     int dev = 0, cus = 0;
@@ -1129,6 +1142,7 @@ vinf_status launch_dda(const void* q, const void* k, const void* v, const void* 
     g.nstrips = S * heads;
     g.nchunks = g.nfull = g.nitems = 0;
     g.sl2e = scale * 1.4426950408889634f;
+    g.chunk_major = q == k && k == v && n_local > 0 && n_global > 0;
     if (dt == VINF_BF16) {
         // Remainder packing: r = nq % 256 leftover queries per strip go M strips
         // to an item when they fit M slices (M = 1: one partial item per strip).
