@@ -196,6 +196,28 @@ def test_attention_scale_and_determinism():
     check(fetch(o3), ref, BF, "scale 0.05")
 
 
+@pytest.mark.parametrize("F,H,W,C", [(1024, 8, 5, 320), (300, 7, 3, 128), (2300, 2, 3, 192), (40, 5, 4, 64)])
+def test_attention_item_orders_agree(F, H, W, C):
+    """One tensor passed as q, k and v (the chain's case) takes the chunk-major
+    item order; the same values in three buffers take the strip-major ranges.
+    Each item is computed once in either order, so the outputs agree bit for
+    bit; so do the one-sided key sets, which take the strip-major ranges both
+    times, and both full-key outputs match the oracle at sampled locations."""
+    announce(f"attention item orders F={F} H={H} W={W} C={C}")
+    xh = rnd((F, H, W, C), 91, BF)
+    x = upload(xh)
+    k, v = x.clone(), x.clone()
+    o1 = vinf.dual_domain_attn(x, x, x)
+    o2 = vinf.dual_domain_attn(x, k, v)
+    assert np.array_equal(bits(o1), bits(o2))
+    for nl, ng in ((16, 0), (0, 16)):
+        a1 = vinf.dual_domain_attn(x, x, x, n_local=nl, n_global=ng)
+        a2 = vinf.dual_domain_attn(x, k, v, n_local=nl, n_global=ng)
+        assert np.array_equal(bits(a1), bits(a2))
+    locs = sample_locs(H * W, 3, seed=F)
+    check(fetch(o1, locs), oracle.dda(xh, xh, xh, locs=locs), BF, "item orders, sampled")
+
+
 # ------------------------------------------------------------- full workloads
 
 CFG = synth.CONFIGS
