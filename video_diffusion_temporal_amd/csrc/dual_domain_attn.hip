@@ -57,7 +57,9 @@
 //   * Item order: items are numbered strip-major (a strip's frame chunks in
 //     a row) and every workgroup takes a contiguous range, so consecutive
 //     items of a workgroup are neighbouring chunks of one strip whose shared
-//     window frames come from L2.
+//     window frames come from L2; when q, k and v are one tensor and the
+//     key set is full, workgroups take chunk-major items round-robin
+//     instead (measured faster there).
 //   * Pipelining: one persistent 512-thread workgroup per CU owns two LDS
 //     buffers (2 x 80 KB).  Its two 256-thread halves alternate: while one
 //     half stages its next work item (HBM -> LDS, plus its q rows into
@@ -655,7 +657,7 @@ __device__ __forceinline__ void dda_compute(const char* __restrict__ buf, uint16
     // frame 4a + k%4, chunk b + 4*(k/4))
     const int tg = it.t0 + (lt & ~3);
     if (tg + 3 < tend) {
-        // every frame of the quad is a query (all but the video's last
+        // every frame of the quad is a query (all but the queries' last
         // quad): 8 stores from one address, no branch per store
         uint16_t* ob = o + (int64_t)(tg - g.f0) * rs + col + lb * 8;
 #pragma unroll
